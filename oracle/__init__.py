@@ -1,0 +1,206 @@
+"""CPU oracle for the QLoRA NF4 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+The plain, slow, obviously-correct definition that the HIP library is checked
+against (C source in ``oracle.c``).  Only ``tests/``, ``__graft_entry__.smoke``
+and the CPU-baseline leg of ``bench.py`` may import this package; the product
+path (``bit_nf4_quantized_17_amd``) never does, and the two share no code.
+
+Every wrapper here is argument marshalling (numpy arrays <-> C pointers); the
+arithmetic is all in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+          "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm", "-lpthread"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        D = ctypes.c_double
+        L.oracle_nf4_levels.argtypes = [P]
+        L.oracle_nf4_levels.restype = None
+        L.oracle_normal_quantile.argtypes = [D]
+        L.oracle_normal_quantile.restype = D
+        L.oracle_nearest_level.argtypes = [ctypes.c_float, P]
+        L.oracle_nearest_level.restype = I
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = D
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_encode_blocks.argtypes = [P, I64, I64, P, P, P, I]
+        L.oracle_encode_blocks.restype = I
+        L.oracle_nf4_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P, I]
+        L.oracle_nf4_quantize.restype = I
+        L.oracle_nf4_dequantize.argtypes = [P, P, P, I64, I64, P, I]
+        L.oracle_nf4_dequantize.restype = I
+        L.oracle_qlora_fwd.argtypes = [P, I64, I64, P, I64, P, P, I, D, P, I64, P, P, I]
+        L.oracle_qlora_fwd.restype = I
+        L.oracle_qlora_bwd_dx.argtypes = [P, I64, I64, P, I64, P, P, I, D, P, I64, P, I]
+        L.oracle_qlora_bwd_dx.restype = I
+        L.oracle_qlora_bwd_adapters.argtypes = [I64, I64, P, P, I64, P, P, I, D, P, P, I]
+        L.oracle_qlora_bwd_adapters.restype = I
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def nf4_levels() -> np.ndarray:
+    out = np.zeros(16, np.float32)
+    lib().oracle_nf4_levels(_ptr(out))
+    return out
+
+
+def normal_quantile(p: float) -> float:
+    return lib().oracle_normal_quantile(p)
+
+
+def nearest_level(v: float, levels: np.ndarray) -> int:
+    lv = np.ascontiguousarray(levels, np.float32)
+    return lib().oracle_nearest_level(v, _ptr(lv))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().oracle_e4m3_encode(v)
+
+
+def bf16_rne(f: float) -> int:
+    return lib().oracle_bf16_rne(f)
+
+
+def encode_blocks(W: np.ndarray, levels: np.ndarray, threads: int | None = None):
+    """(codes uint8 [N*K/2], absmax fp32 [N*K/64]) with a caller-given table."""
+    W = np.ascontiguousarray(W, np.float32)
+    rows, cols = W.shape
+    lv = np.ascontiguousarray(levels, np.float32)
+    codes = np.zeros(rows * cols // 2, np.uint8)
+    absmax = np.zeros(rows * cols // 64, np.float32)
+    _check(lib().oracle_encode_blocks(_ptr(W), rows, cols, _ptr(lv), _ptr(codes), _ptr(absmax),
+                                      threads or default_threads()), "encode_blocks")
+    return codes, absmax
+
+
+def nf4_quantize(W: np.ndarray, block: int = 64, dq_block: int = 256, threads: int | None = None):
+    """(codes, qscale, dscale, absmax) for a fp32 [N, K] weight."""
+    W = np.ascontiguousarray(W, np.float32)
+    rows, cols = W.shape
+    nb = rows * cols // 64
+    ng = (nb + 255) // 256
+    codes = np.zeros(rows * cols // 2, np.uint8)
+    qscale = np.zeros(nb, np.uint8)
+    dscale = np.zeros(ng, np.float32)
+    absmax = np.zeros(nb, np.float32)
+    _check(lib().oracle_nf4_quantize(_ptr(W), rows, cols, block, dq_block, _ptr(codes),
+                                     _ptr(qscale), _ptr(dscale), _ptr(absmax),
+                                     threads or default_threads()), "nf4_quantize")
+    return codes, qscale, dscale, absmax
+
+
+def nf4_dequantize(codes, qscale, dscale, rows: int, cols: int, threads: int | None = None):
+    """bf16 bit patterns (uint16 [N, K])."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    qscale = np.ascontiguousarray(qscale, np.uint8)
+    dscale = np.ascontiguousarray(dscale, np.float32)
+    out = np.zeros((rows, cols), np.uint16)
+    _check(lib().oracle_nf4_dequantize(_ptr(codes), _ptr(qscale), _ptr(dscale), rows, cols,
+                                       _ptr(out), threads or default_threads()), "nf4_dequantize")
+    return out
+
+
+def _u16(a):
+    return np.ascontiguousarray(a, np.uint16)
+
+
+def qlora_fwd(Wdq, X, A, B, alpha: float, rows=None, threads: int | None = None):
+    """(Y [n, N] double, T [n, r] double) for the listed rows of X (all if None).
+    All matrix inputs are bf16 bit patterns (uint16)."""
+    Wdq, X, A, B = _u16(Wdq), _u16(X), _u16(A), _u16(B)
+    N, K = Wdq.shape
+    M = X.shape[0]
+    r = A.shape[0]
+    idx = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    n = M if idx is None else idx.size
+    Y = np.zeros((n, N), np.float64)
+    T = np.zeros((n, r), np.float64)
+    _check(lib().oracle_qlora_fwd(_ptr(Wdq), N, K, _ptr(X), M, _ptr(A), _ptr(B), r, alpha,
+                                  _ptr(idx), n, _ptr(Y), _ptr(T), threads or default_threads()),
+           "qlora_fwd")
+    return Y, T
+
+
+def qlora_bwd_dx(Wdq, dY, A, B, alpha: float, rows=None, threads: int | None = None):
+    Wdq, dY, A, B = _u16(Wdq), _u16(dY), _u16(A), _u16(B)
+    N, K = Wdq.shape
+    M = dY.shape[0]
+    r = A.shape[0]
+    idx = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    n = M if idx is None else idx.size
+    dX = np.zeros((n, K), np.float64)
+    _check(lib().oracle_qlora_bwd_dx(_ptr(Wdq), N, K, _ptr(dY), M, _ptr(A), _ptr(B), r, alpha,
+                                     _ptr(idx), n, _ptr(dX), threads or default_threads()),
+           "qlora_bwd_dx")
+    return dX
+
+
+def qlora_bwd_adapters(X, dY, A, B, alpha: float, want_dA=True, want_dB=True,
+                       threads: int | None = None):
+    X, dY, A, B = _u16(X), _u16(dY), _u16(A), _u16(B)
+    M, K = X.shape
+    N = dY.shape[1]
+    r = A.shape[0]
+    dA = np.zeros((r, K), np.float64) if want_dA else None
+    dB = np.zeros((N, r), np.float64) if want_dB else None
+    _check(lib().oracle_qlora_bwd_adapters(N, K, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, alpha,
+                                           _ptr(dA), _ptr(dB), threads or default_threads()),
+           "qlora_bwd_adapters")
+    return dA, dB

@@ -1,0 +1,106 @@
+/*
+ * oracle.h -- the CPU oracle for the QLoRA NF4 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
+ * definition the HIP library is checked against.  Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the product path
+ * never does.  It shares no code, header, table or helper with the HIP
+ * library under bit_nf4_quantized_17_amd/.
+ *
+ * Sources (the pages this follows):
+ *  - Ultralytics glossary "QLoRA", section "How QLoRA works": the NF4 bullet
+ *    (one 4-bit code per weight, 16 levels at normal quantiles, one absmax
+ *    scale per block of 64), the double-quantization bullet (block scales
+ *    re-quantized to 8 bits in blocks of 256), the paragraph on the forward
+ *    and backward passes, and the code snippet that builds the NF4 levels and
+ *    encodes by nearest level.
+ *  - vnread "Grokking QLoRA", section "Double Quantization": the 8-bit format
+ *    of the second level is FP8.
+ *  - IBM "What is LoRA?" (PEFT parameters: r, lora_alpha as the scaling
+ *    factor) and ezsol "Mastering model fine-tuning", section on LoRA
+ *    (Delta W = B A).
+ *
+ * Conventions (all arrays host memory, row-major, caller-owned):
+ *  W        fp32 [rows=N][cols=K]; blocks of 64 run along a row (K % 64 == 0)
+ *  codes    uint8 [N*K/2]; byte e/2 holds element e; even e in the low nibble
+ *  qscale   uint8 [N*K/64]; OCP FP8 E4M3 code of each block's scale
+ *  dscale   fp32 [ceil(nb/256)]; second-level constant per group of 256 blocks
+ *  bf16     passed as uint16 bit patterns
+ *  results of the fwd/bwd definitions are returned in double.
+ *
+ * Return value of every int function: 0 on success, negative on bad input.
+ */
+#ifndef QLORA_NF4_ORACLE_H
+#define QLORA_NF4_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The 16 NF4 levels in code order, each the exact formula rounded once to fp32. */
+void oracle_nf4_levels(float out[16]);
+
+/* Standard normal quantile, evaluated in double by bisection on erfc. */
+double oracle_normal_quantile(double p);
+
+/* Nearest-level code of v among 16 sorted levels: argmin_i fl32(|v - L[i]|),
+ * first minimum (lower code) on ties. */
+int oracle_nearest_level(float v, const float levels[16]);
+
+/* OCP FP8 E4M3FN: value of a code, and round-to-nearest-even encode of a
+ * non-negative float (saturating at 448). */
+double oracle_e4m3_value(uint8_t code);
+uint8_t oracle_e4m3_encode(float v);
+
+/* fp32 -> bf16 round-to-nearest-even (bit pattern). */
+uint16_t oracle_bf16_rne(float f);
+
+/* Blockwise absmax + nearest-level encode + pack with a caller-given level
+ * table (the NF4 table, or any 16 sorted levels), no double quantization.
+ * absmax_out [N*K/64] is filled when non-NULL. */
+int oracle_encode_blocks(const float* W, int64_t rows, int64_t cols,
+                         const float levels[16], uint8_t* codes, float* absmax_out,
+                         int nthreads);
+
+/* Full NF4 quantization: absmax per 64, encode, pack, double-quantize the
+ * block scales to E4M3 in groups of 256. */
+int oracle_nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
+                        uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
+                        int nthreads);
+
+/* Dequantize to bf16: w' = bf16(fl32(L[code] * fl32(E4M3(q) * d))). */
+int oracle_nf4_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
+                          int64_t rows, int64_t cols, uint16_t* out_bf16, int nthreads);
+
+/* Forward, for the rows listed in row_idx (or all M rows if row_idx == NULL):
+ *   T[m,j] = sum_k X[m,k] A[j,k]
+ *   Y[m,n] = sum_k X[m,k] W'[n,k] + (alpha/r) sum_j T[m,j] B[n,j]
+ * W' is given as the dequantized bf16 weight [N][K].
+ * Y_out [n_out][N], T_out [n_out][r] (T_out may be NULL). */
+int oracle_qlora_fwd(const uint16_t* Wdq, int64_t N, int64_t K,
+                     const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                     int r, double alpha, const int64_t* row_idx, int64_t n_rows,
+                     double* Y_out, double* T_out, int nthreads);
+
+/* Backward dX for the listed rows (or all rows):
+ *   U[m,j]  = sum_n dY[m,n] B[n,j]
+ *   dX[m,k] = sum_n dY[m,n] W'[n,k] + (alpha/r) sum_j U[m,j] A[j,k]          */
+int oracle_qlora_bwd_dx(const uint16_t* Wdq, int64_t N, int64_t K,
+                        const uint16_t* dY, int64_t M, const uint16_t* A, const uint16_t* B,
+                        int r, double alpha, const int64_t* row_idx, int64_t n_rows,
+                        double* dX_out, int nthreads);
+
+/* Adapter gradients in full (only the adapters are trained):
+ *   dA[j,k] = (alpha/r) sum_m U[m,j] X[m,k]
+ *   dB[n,j] = (alpha/r) sum_m dY[m,n] T[m,j]
+ * with T = X A^T and U = dY B computed here in double.  Either output may be NULL. */
+int oracle_qlora_bwd_adapters(int64_t N, int64_t K, const uint16_t* X, const uint16_t* dY,
+                              int64_t M, const uint16_t* A, const uint16_t* B, int r,
+                              double alpha, double* dA_out, double* dB_out, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

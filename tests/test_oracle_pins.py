@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print, closed forms, an independent library routine, high-precision
+evaluation, exhaustive or brute-force checks, or identities of the linear
+algebra.  A plausible slip anywhere in the oracle (a dropped term, a wrong
+sign, index or transposition, a wrong scale) fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_bits(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# O1: the NF4 table (Ultralytics "QLoRA", "How QLoRA works", the snippet)
+# --------------------------------------------------------------------------
+def _levels_from_quantile(q):
+    """16 NF4 levels from a given quantile function, rounded once to fp32."""
+    off = 0.9677083
+    pos = [q(off + (0.5 - off) * i / 8) for i in range(8)]
+    neg = [-q(off + (0.5 - off) * i / 7) for i in range(7)]
+    v = sorted(pos + neg + [0.0])
+    return np.array([float(x / v[-1]) for x in v], np.float32)
+
+
+def test_table_matches_mpmath_50_digits(orc):
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+
+    def q(p):
+        return mpmath.sqrt(2) * mpmath.erfinv(2 * mpmath.mpf(p) - 1)
+
+    off = mpmath.mpf("0.9677083")
+    pos = [q(off + (mpmath.mpf("0.5") - off) * i / 8) for i in range(8)]
+    neg = [-q(off + (mpmath.mpf("0.5") - off) * i / 7) for i in range(7)]
+    v = sorted(pos + neg + [mpmath.mpf(0)])
+    ref = np.array([float(x / v[-1]) for x in v], np.float32)
+    got = orc.nf4_levels()
+    assert [f32_bits(x) for x in got] == [f32_bits(x) for x in ref]
+
+
+def test_table_matches_statistics_normaldist(orc):
+    from statistics import NormalDist
+    ref = _levels_from_quantile(NormalDist().inv_cdf)
+    got = orc.nf4_levels()
+    assert [f32_bits(x) for x in got] == [f32_bits(x) for x in ref]
+
+
+def test_table_invariants(orc):
+    L = orc.nf4_levels()
+    assert L.dtype == np.float32 and L.shape == (16,)
+    assert np.all(np.diff(L.astype(np.float64)) > 0), "strictly increasing"
+    assert L[0] == -1.0 and L[15] == 1.0
+    assert L[7] == 0.0 and f32_bits(L[7]) == 0, "an exact +0 level at code 7"
+    assert int(np.sum(L < 0)) == 7 and int(np.sum(L > 0)) == 8
+    # normaliser: the largest quantile is Phi^-1(0.9677083)
+    assert orc.normal_quantile(0.9677083) == pytest.approx(1.8481309597573738, rel=1e-14)
+    # minimum gap (codes 7->8, 0.0796) and maximum gap (codes 0->1, 0.3038)
+    gaps = np.diff(L.astype(np.float64))
+    assert int(np.argmin(gaps)) == 7 and int(np.argmax(gaps)) == 0
+
+
+def test_table_close_to_snippet_in_torch_float32(orc):
+    """The page's own construction in torch float32 (its erfinv) lands within 5 ulp."""
+    torch = pytest.importorskip("torch")
+    normal = torch.distributions.Normal(0.0, 1.0)
+    p_pos = torch.linspace(0.9677083, 0.5, 9)[:-1]
+    p_neg = torch.linspace(0.9677083, 0.5, 8)[:-1]
+    t = torch.cat([-normal.icdf(p_neg), torch.zeros(1), normal.icdf(p_pos)]).sort().values
+    t = (t / t.max()).numpy()
+    got = orc.nf4_levels()
+    ulps = np.abs(t.view(np.int32).astype(np.int64) - got.view(np.int32).astype(np.int64))
+    assert int(ulps.max()) <= 5
+
+
+# --------------------------------------------------------------------------
+# O2-O5: encode
+# --------------------------------------------------------------------------
+def test_snippet_printed_mse(orc):
+    """Ultralytics "QLoRA": the snippet prints NF4 MSE 3.395e-06 and 4.053e-06 for
+    16 evenly spaced levels, on torch.manual_seed(0) randn(4096, 64) * 0.02."""
+    torch = pytest.importorskip("torch")
+    gold = json.load(open(os.path.join(GOLDEN, "snippet_mse.json")))
+    torch.manual_seed(0)
+    w = (torch.randn(4096, 64) * 0.02).numpy()
+    absmax = np.abs(w).max(axis=1, keepdims=True)
+    for levels, key in ((orc.nf4_levels(), "nf4_mse_printed"),
+                        (torch.linspace(-1, 1, 16).numpy(), "int4_mse_printed")):
+        codes, am = orc.encode_blocks(w, levels)
+        assert np.array_equal(am, absmax[:, 0])
+        c = np.empty(w.size, np.int64)
+        c[0::2] = codes & 15
+        c[1::2] = codes >> 4
+        restored = levels[c].reshape(w.shape) * absmax          # fp32 products
+        mse = float(np.mean((restored - w).astype(np.float64) ** 2))
+        assert f"{mse:.3e}" == gold[key], (key, mse)
+
+
+def test_self_codes(orc):
+    """Encoding each level (times the block absmax) returns its own code."""
+    L = orc.nf4_levels()
+    for e in (-20, -7, -3, 0, 5, 30):
+        block = np.tile(L, 4).astype(np.float32) * np.float32(2.0 ** e)   # absmax = 2^e
+        codes, am = orc.encode_blocks(block.reshape(1, 64), L)
+        assert am[0] == np.float32(2.0 ** e)
+        c = np.empty(64, np.int64)
+        c[0::2], c[1::2] = codes & 15, codes >> 4
+        assert list(c) == list(range(16)) * 4
+
+
+def test_exact_ties_take_lower_code(orc):
+    """The listed values are exact fp32 ties (checked with numpy float32) and
+    encode to the lower code, as argmin does."""
+    L = orc.nf4_levels()
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "nf4_ties.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 5
+    for j, h, _ in rows:
+        j = int(j)
+        v = np.array([int(h, 16)], np.uint32).view(np.float32)[0]
+        assert np.abs(v - L[j]) == np.abs(L[j + 1] - v)
+        assert orc.nearest_level(float(v), L) == j
+        # one ulp either side decides for the nearer level
+        up = np.nextafter(v, np.float32(2)); dn = np.nextafter(v, np.float32(-2))
+        assert {orc.nearest_level(float(up), L), orc.nearest_level(float(dn), L)} == {j, j + 1}
+
+
+def test_nearest_level_matches_exact_rational_rule(orc):
+    """Away from the five exact fp32 ties, the fp32-distance argmin equals the
+    nearest level in exact rational arithmetic."""
+    L = orc.nf4_levels()
+    Lq = [Fraction(float(x)) for x in L]
+    ties = {int(ln.split()[1], 16) for ln in open(os.path.join(GOLDEN, "nf4_ties.txt"))
+            if ln.strip() and not ln.startswith("#")}
+    rng = np.random.default_rng(123)
+    v = np.concatenate([rng.uniform(-1, 1, 4000).astype(np.float32),
+                        # values within a few ulps of each midpoint
+                        np.concatenate([np.float32((float(L[j]) + float(L[j + 1])) / 2) +
+                                        np.arange(-6, 7, dtype=np.float32) *
+                                        np.spacing(np.float32(abs(L[j]) + abs(L[j + 1])))
+                                        for j in range(15)]).astype(np.float32)])
+    for x in v:
+        if int(np.float32(x).view(np.uint32)) in ties:
+            continue
+        xq = Fraction(float(x))
+        ref = min(range(16), key=lambda i: (abs(xq - Lq[i]), i))
+        assert orc.nearest_level(float(x), L) == ref, x
+
+
+def test_pack_nibble_order_and_all_zero_block(orc):
+    """Two codes per byte, element e of the flattened row in byte e/2, even e in
+    the low nibble; an all-zero block gets the exact-zero code 7."""
+    L = orc.nf4_levels()
+    want = [(3 * e + 5) % 16 for e in range(64)]
+    row = np.array([L[c] for c in want], np.float32) * np.float32(0.75)
+    row[want.index(0)] = np.float32(-0.75)     # a code-0 element: absmax 0.75
+    W = np.stack([row, np.zeros(64, np.float32)])
+    codes, am = orc.encode_blocks(W.reshape(1, 128), L)
+    assert am[0] == np.float32(0.75) and am[1] == 0
+    expect = bytes((want[2 * i] | (want[2 * i + 1] << 4)) for i in range(32))
+    assert bytes(codes[:32]) == expect
+    assert bytes(codes[32:]) == bytes([0x77] * 32)
+    qc, qs, ds, _ = orc.nf4_quantize(np.zeros((1, 64), np.float32))
+    assert bytes(qc) == bytes([0x77] * 32) and qs[0] == 0 and ds[0] == 0
+    deq = orc.nf4_dequantize(qc, qs, ds, 1, 64)
+    assert np.all(deq == 0)
+
+
+# --------------------------------------------------------------------------
+# O6: double quantization (E4M3 in groups of 256)
+# --------------------------------------------------------------------------
+def test_e4m3_values_match_torch(orc):
+    torch = pytest.importorskip("torch")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = codes.to(torch.float64).numpy()
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            assert math.isnan(ref[c])
+            continue
+        assert orc.e4m3_value(c) == ref[c], c
+
+
+def test_e4m3_encode_matches_torch(orc):
+    torch = pytest.importorskip("torch")
+    vals = [orc.e4m3_value(c) for c in range(0x7F)]
+    mids = [(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])]
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([np.array(vals, np.float32), np.array(mids, np.float32),
+                         np.nextafter(np.array(mids, np.float32), np.float32(0)),
+                         np.nextafter(np.array(mids, np.float32), np.float32(1e9)),
+                         rng.uniform(0, 448, 20000).astype(np.float32),
+                         np.exp2(rng.uniform(-14, 8.8, 20000)).astype(np.float32),
+                         np.array([0.0, 448.0, np.float32(448.0) * np.float32(1 + 2**-23)],
+                                  np.float32)])
+    xs = xs[xs <= np.float32(448.0) * np.float32(1 + 2**-22)]
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(float(x)) for x in xs], np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(xs[i], got[i], ref[i]) for i in bad[:5]]
+
+
+def test_bf16_rne_matches_torch(orc):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    u = rng.integers(0, 2**32, 50000, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]                     # finite only
+    ties = (rng.integers(0, 2**16, 2000, dtype=np.uint32) << 16) | 0x8000
+    ties = ties[((ties >> 23) & 0xFF) != 0xFF]
+    xs = np.concatenate([u, ties.astype(np.uint32)]).view(np.float32)
+    ref = torch.from_numpy(xs.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.bf16_rne(float(x)) for x in xs], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_double_quant_structure(orc):
+    """Per group of 256 blocks the largest scale maps to E4M3 max (code 0x7E,
+    value 448); every restored scale is within E4M3's half-ulp (2^-4 relative)
+    of the exact absmax; the last group may be short."""
+    cfg = si.custom(N=64 * 3, K=192, M=1, r=8, outlier_frac=0.01, seed=3)   # 576 blocks
+    W = si.weight(cfg, 0)
+    codes, qs, ds, am = orc.nf4_quantize(W)
+    nb = W.size // 64
+    assert qs.size == nb and ds.size == (nb + 255) // 256 == 3
+    for g in range(ds.size):
+        b0, b1 = 256 * g, min(256 * g + 256, nb)
+        c = am[b0:b1].max()
+        assert ds[g] == np.float32(c / np.float32(448.0))
+        assert qs[b0 + int(np.argmax(am[b0:b1]))] == 0x7E
+        restored = np.array([orc.e4m3_value(int(q)) for q in qs[b0:b1]]) * float(ds[g])
+        rel = np.abs(restored - am[b0:b1].astype(np.float64)) / am[b0:b1]
+        assert rel.max() <= 2.0 ** -4 + 1e-7
+
+
+def test_storage_footprint_closed_forms(orc):
+    """Ultralytics "QLoRA" and vnread "Grokking QLoRA": 0.5 -> ~0.127 bits/param,
+    ~0.37 saved, ~3 GB at 65B, ~130 GB at 16 bit, NF4 ~33 GB, NF4+DQ ~34 GB."""
+    g = json.load(open(os.path.join(GOLDEN, "storage_footprint.json")))
+    W = np.zeros((256, 4096), np.float32)   # 16384 blocks, 64 groups
+    codes, qs, ds, _ = orc.nf4_quantize(W)
+    n = W.size
+    bits_dq = 8 * (qs.nbytes + ds.nbytes) / n
+    bits_nodq = 32 * (n // 64) / n
+    assert bits_nodq == g["no_dq_overhead_bits_per_param"]
+    assert bits_dq == pytest.approx(8 / 64 + 32 / (64 * 256))
+    assert round(bits_dq, 3) == g["dq_overhead_bits_per_param"]
+    assert round(bits_nodq - bits_dq, 2) == g["dq_saving_bits_per_param"]
+    P = g["params_65b"]
+    assert round((bits_nodq - bits_dq) * P / 8 / 1e9) == g["dq_saving_gb_65b"]
+    assert round(16 * P / 8 / 1e9) == g["fp16_gb_65b"]
+    nf4_total_gb = (8 * codes.nbytes / n + bits_dq) * P / 8 / 1e9
+    assert math.floor(4 * P / 8 / 1e9) >= g["nf4_gb_65b_low"] - 1
+    assert round(nf4_total_gb) == g["nf4_dq_gb_65b"]
+
+
+# --------------------------------------------------------------------------
+# O7: dequantize
+# --------------------------------------------------------------------------
+def test_dequant_error_bound(orc):
+    """|w' - w| <= (largest half-gap between levels) * restored scale + scale error
+    + bf16 half-ulp; and the dequantized value has the sign of its level."""
+    cfg = si.custom(N=128, K=256, M=1, r=8, seed=5)
+    W = si.weight(cfg, 0)
+    codes, qs, ds, am = orc.nf4_quantize(W)
+    deq = si.bf16_bits_to_f32(orc.nf4_dequantize(codes, qs, ds, *W.shape)).astype(np.float64)
+    L = orc.nf4_levels().astype(np.float64)
+    half_gap = np.max(np.diff(L)) / 2
+    a = np.repeat(am.astype(np.float64), 64).reshape(W.shape)
+    sc = np.repeat(np.array([orc.e4m3_value(int(q)) for q in qs]) *
+                   np.repeat(ds.astype(np.float64), 256)[:qs.size], 64).reshape(W.shape)
+    bound = half_gap * a + np.abs(sc - a) + np.abs(deq) * 2.0 ** -8
+    assert np.all(np.abs(deq - W) <= bound + 1e-12)
+    c = np.empty(W.size, np.int64)
+    c[0::2], c[1::2] = codes & 15, codes >> 4
+    lv = L[c].reshape(W.shape)
+    assert np.all(np.sign(deq) == np.sign(lv))
+
+
+# --------------------------------------------------------------------------
+# O8-O9: forward and backward, pinned by identities of the linear algebra
+# --------------------------------------------------------------------------
+def _small_problem(orc, N=48, K=128, M=5, r=4, alpha=8.0, seed=2):
+    cfg = si.custom(N=N, K=K, M=M, r=r, alpha=alpha, seed=seed)
+    W = si.weight(cfg, 0)
+    codes, qs, ds, _ = orc.nf4_quantize(W)
+    Wdq = orc.nf4_dequantize(codes, qs, ds, N, K)
+    X = si.activations(cfg, 0)
+    A, B = si.adapters(cfg, 0)
+    dY = si.upstream(cfg, 0)
+    return cfg, Wdq, X, A, B, dY
+
+
+def _f(h):
+    return si.bf16_bits_to_f32(h).astype(np.float64)
+
+
+def test_forward_equals_merged_weight_matmul(orc):
+    """Y = X (W' + (alpha/r) B A)^T, evaluated with numpy's float64 matmul."""
+    cfg, Wdq, X, A, B, dY = _small_problem(orc)
+    Y, T = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha)
+    s = cfg.alpha / cfg.r
+    ref = _f(X) @ (_f(Wdq) + s * _f(B) @ _f(A)).T
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(T, _f(X) @ _f(A).T, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_rows_subset_and_alpha_linearity(orc):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc)
+    Y, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha)
+    Ys, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha, rows=[4, 0, 2])
+    assert np.array_equal(Ys, Y[[4, 0, 2]])
+    Y0, _ = orc.qlora_fwd(Wdq, X, A, B, 0.0)
+    Y2, _ = orc.qlora_fwd(Wdq, X, A, B, 2 * cfg.alpha)
+    np.testing.assert_allclose(Y2 - Y, Y - Y0, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(Y0, _f(X) @ _f(Wdq).T, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_B_gives_base_output_and_zero_dA(orc):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc)
+    Bz = np.zeros_like(B)
+    Y, _ = orc.qlora_fwd(Wdq, X, A, Bz, cfg.alpha)
+    Y0, _ = orc.qlora_fwd(Wdq, X, A, B, 0.0)
+    assert np.array_equal(Y, Y0)
+    dA, dB = orc.qlora_bwd_adapters(X, dY, A, Bz, cfg.alpha)
+    assert np.all(dA == 0)
+    np.testing.assert_allclose(dB, cfg.alpha / cfg.r * _f(dY).T @ (_f(X) @ _f(A).T),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_zero_A_gives_zero_dB(orc):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc)
+    dA, dB = orc.qlora_bwd_adapters(X, dY, np.zeros_like(A), B, cfg.alpha)
+    assert np.all(dB == 0)
+    np.testing.assert_allclose(dA, cfg.alpha / cfg.r * (_f(dY) @ _f(B)).T @ _f(X),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_backward_adjoint_identities(orc):
+    """Y is linear in X, in A and in B: <dY, Y(X)> = <dX, X>, and
+    <dA, A> = <dB, B> = <dY, Y - Y_base>."""
+    cfg, Wdq, X, A, B, dY = _small_problem(orc)
+    Y, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha)
+    Yb, _ = orc.qlora_fwd(Wdq, X, A, B, 0.0)
+    dX = orc.qlora_bwd_dx(Wdq, dY, A, B, cfg.alpha)
+    dA, dB = orc.qlora_bwd_adapters(X, dY, A, B, cfg.alpha)
+    g = _f(dY)
+    lhs = float(np.sum(g * Y))
+    assert lhs == pytest.approx(float(np.sum(dX * _f(X))), rel=1e-10)
+    lora = float(np.sum(g * (Y - Yb)))
+    assert float(np.sum(dA * _f(A))) == pytest.approx(lora, rel=1e-9)
+    assert float(np.sum(dB * _f(B))) == pytest.approx(lora, rel=1e-9)
+
+
+def test_backward_secants(orc):
+    """L = <dY, Y> is linear in each input element, so a secant through two exact
+    bf16 values of one element equals that element's gradient."""
+    cfg, Wdq, X, A, B, dY = _small_problem(orc, N=24, K=64, M=3, r=3)
+    g = _f(dY)
+    dX = orc.qlora_bwd_dx(Wdq, dY, A, B, cfg.alpha)
+    dA, dB = orc.qlora_bwd_adapters(X, dY, A, B, cfg.alpha)
+    one, half = np.uint16(0x3F80), np.uint16(0xBF00)     # +1.0 and -0.5 in bf16
+
+    def L(Xm, Am, Bm):
+        Y, _ = orc.qlora_fwd(Wdq, Xm, Am, Bm, cfg.alpha)
+        return float(np.sum(g * Y))
+
+    for (name, arr, grad, idx) in (("X", X, dX, (1, 17)), ("A", A, dA, (2, 40)),
+                                   ("B", B, dB, (13, 1)), ("X", X, dX, (2, 63))):
+        a1, a2 = arr.copy(), arr.copy()
+        a1[idx], a2[idx] = one, half
+        args1 = {"X": X, "A": A, "B": B}; args1[name] = a1
+        args2 = {"X": X, "A": A, "B": B}; args2[name] = a2
+        sec = (L(args1["X"], args1["A"], args1["B"]) - L(args2["X"], args2["A"], args2["B"])) / 1.5
+        assert sec == pytest.approx(float(grad[idx]), rel=1e-9, abs=1e-9), name
+
+
+def test_dx_rows_subset(orc):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc)
+    dX = orc.qlora_bwd_dx(Wdq, dY, A, B, cfg.alpha)
+    dXs = orc.qlora_bwd_dx(Wdq, dY, A, B, cfg.alpha, rows=[3, 1])
+    assert np.array_equal(dXs, dX[[3, 1]])
+    s = cfg.alpha / cfg.r
+    ref = _f(dY) @ (_f(Wdq) + s * _f(B) @ _f(A))
+    np.testing.assert_allclose(dX, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_results_do_not_depend_on_thread_count(orc):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc, N=40, K=192, M=7, r=5)
+    W = si.weight(cfg, 0)
+    q1 = orc.nf4_quantize(W, threads=1)
+    q7 = orc.nf4_quantize(W, threads=7)
+    for a, b in zip(q1, q7):
+        assert np.array_equal(a, b)
+    y1, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha, threads=1)
+    y3, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha, threads=3)
+    assert np.array_equal(y1, y3)
