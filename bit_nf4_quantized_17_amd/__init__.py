@@ -1,0 +1,227 @@
+"""MI355X (gfx950) QLoRA NF4 linear layer -- Python binding of libqlora_nf4.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libqlora_nf4.so`` behind the C ABI of ``include/qlora_nf4.h``.  PyTorch is
+used for device memory and the current HIP stream.  There is no fallback: if
+the library is missing or fails to load, every call raises.
+
+Functions keep the C ABI's names:
+  nf4_levels, nf4_storage_bytes, nf4_quantize, nf4_dequantize,
+  qlora_fwd_workspace_bytes, qlora_linear_fwd,
+  qlora_bwd_workspace_bytes, qlora_linear_bwd, qlora_abi_version
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+
+QL_DTYPE_BF16 = 1
+QLORA_MAX_RANK = 128
+_STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_UNSUPPORTED",
+           -4: "QL_ERR_ALIGN", -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
+
+_lib = None
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
+                ("dscale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqlora_nf4.so (built by build.py); raises if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m bit_nf4_quantized_17_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    WP = ctypes.POINTER(_Weight)
+    L.qlora_abi_version.argtypes, L.qlora_abi_version.restype = [], I
+    L.qlora_last_error.argtypes, L.qlora_last_error.restype = [], ctypes.c_char_p
+    L.nf4_levels.argtypes, L.nf4_levels.restype = [P], None
+    L.nf4_storage_bytes.argtypes = [I64, I64, I, I, P, P, P]
+    L.nf4_storage_bytes.restype = I
+    L.nf4_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P, P]
+    L.nf4_quantize.restype = I
+    L.nf4_dequantize.argtypes = [WP, P, P]
+    L.nf4_dequantize.restype = I
+    L.qlora_fwd_workspace_bytes.argtypes = [I64, I64, I64, I]
+    L.qlora_fwd_workspace_bytes.restype = SZ
+    L.qlora_linear_fwd.argtypes = [WP, P, I64, P, P, I, F, I, P, P, P, SZ, P]
+    L.qlora_linear_fwd.restype = I
+    L.qlora_bwd_workspace_bytes.argtypes = [I64, I64, I64, I]
+    L.qlora_bwd_workspace_bytes.restype = SZ
+    L.qlora_linear_bwd.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P, SZ, P]
+    L.qlora_linear_bwd.restype = I
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise QLoRAError(rc, lib().qlora_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, shape, name):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def qlora_abi_version() -> int:
+    return lib().qlora_abi_version()
+
+
+def nf4_levels():
+    """The 16 fp32 NF4 levels in code order (a list of floats)."""
+    buf = (ctypes.c_float * 16)()
+    lib().nf4_levels(ctypes.cast(buf, ctypes.c_void_p))
+    return list(buf)
+
+
+def nf4_storage_bytes(rows: int, cols: int, block: int = 64, dq_block: int = 256):
+    c, q, d = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().nf4_storage_bytes(rows, cols, block, dq_block, ctypes.byref(c), ctypes.byref(q),
+                                   ctypes.byref(d)))
+    return c.value, q.value, d.value
+
+
+@dataclasses.dataclass
+class NF4Weight:
+    """A quantized frozen weight [rows][cols] held in device tensors."""
+    codes: "torch.Tensor"    # uint8 [rows*cols/2]
+    qscale: "torch.Tensor"   # uint8 [rows*cols/64]
+    dscale: "torch.Tensor"   # float32 [ceil(nb/256)]
+    rows: int
+    cols: int
+
+    def descriptor(self) -> _Weight:
+        return _Weight(self.codes.data_ptr(), self.qscale.data_ptr(), self.dscale.data_ptr(),
+                       self.rows, self.cols, 64, 256)
+
+    @staticmethod
+    def empty(rows: int, cols: int, device="cuda") -> "NF4Weight":
+        import torch
+        c, q, d = nf4_storage_bytes(rows, cols)
+        return NF4Weight(torch.empty(c, dtype=torch.uint8, device=device),
+                         torch.empty(q, dtype=torch.uint8, device=device),
+                         torch.empty(d // 4, dtype=torch.float32, device=device), rows, cols)
+
+
+def nf4_quantize(W, out: Optional[NF4Weight] = None, absmax=None, stream=None) -> NF4Weight:
+    """Quantize a cuda fp32 [rows, cols] weight.  ``absmax`` (optional cuda fp32
+    [rows*cols/64]) receives the exact block scales."""
+    import torch
+    rows, cols = W.shape
+    _need(W, torch.float32, (rows, cols), "W")
+    w = out if out is not None else NF4Weight.empty(rows, cols, W.device)
+    _check(lib().nf4_quantize(W.data_ptr(), rows, cols, 64, 256, w.codes.data_ptr(),
+                              w.qscale.data_ptr(), w.dscale.data_ptr(), _ptr(absmax),
+                              _stream(stream)))
+    return w
+
+
+def nf4_dequantize(w: NF4Weight, out=None, stream=None):
+    """bf16 [rows, cols] dequantized weight."""
+    import torch
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.codes.device)
+    _need(out, torch.bfloat16, (w.rows, w.cols), "out")
+    d = w.descriptor()
+    _check(lib().nf4_dequantize(ctypes.byref(d), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def qlora_fwd_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return lib().qlora_fwd_workspace_bytes(M, N, K, r)
+
+
+def qlora_bwd_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return lib().qlora_bwd_workspace_bytes(M, N, K, r)
+
+
+def _workspace(nbytes: int, device, given):
+    import torch
+    if given is not None:
+        return given
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def qlora_linear_fwd(w: NF4Weight, X, A, B, alpha: float, Y=None, T=None, workspace=None,
+                     stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Y = X W'^T + (alpha/r) (X A^T) B^T ; returns (Y [M, N] bf16, T [M, r] fp32)."""
+    import torch
+    M, K = X.shape
+    r = A.shape[0]
+    N = w.rows
+    _need(X, torch.bfloat16, (M, w.cols), "X")
+    _need(A, torch.bfloat16, (r, K), "A")
+    _need(B, torch.bfloat16, (N, r), "B")
+    Y = Y if Y is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    T = T if T is not None else torch.empty(M, r, dtype=torch.float32, device=X.device)
+    _need(Y, torch.bfloat16, (M, N), "Y")
+    _need(T, torch.float32, (M, r), "T")
+    nbytes = qlora_fwd_workspace_bytes(M, N, K, r)
+    ws = _workspace(nbytes, X.device, workspace)
+    d = w.descriptor()
+    _check(lib().qlora_linear_fwd(ctypes.byref(d), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
+                                  float(alpha), QL_DTYPE_BF16, Y.data_ptr(), T.data_ptr(), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)))
+    return Y, T
+
+
+def qlora_linear_bwd(w: NF4Weight, X, dY, A, B, alpha: float, T=None, want_dX: bool = True,
+                     dX=None, dA=None, dB=None, workspace=None, stream=None):
+    """Returns (dX [M, K] or None, dA [r, K], dB [N, r]) in bf16."""
+    import torch
+    M, K = X.shape
+    r = A.shape[0]
+    N = w.rows
+    _need(X, torch.bfloat16, (M, w.cols), "X")
+    _need(dY, torch.bfloat16, (M, N), "dY")
+    _need(A, torch.bfloat16, (r, K), "A")
+    _need(B, torch.bfloat16, (N, r), "B")
+    if T is not None:
+        _need(T, torch.float32, (M, r), "T")
+    if want_dX and dX is None:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    if dX is not None:
+        _need(dX, torch.bfloat16, (M, K), "dX")
+    dA = dA if dA is not None else torch.empty(r, K, dtype=torch.bfloat16, device=X.device)
+    dB = dB if dB is not None else torch.empty(N, r, dtype=torch.bfloat16, device=X.device)
+    _need(dA, torch.bfloat16, (r, K), "dA")
+    _need(dB, torch.bfloat16, (N, r), "dB")
+    ws = _workspace(qlora_bwd_workspace_bytes(M, N, K, r), X.device, workspace)
+    d = w.descriptor()
+    _check(lib().qlora_linear_bwd(ctypes.byref(d), X.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
+                                  B.data_ptr(), r, float(alpha), QL_DTYPE_BF16, _ptr(T), _ptr(dX),
+                                  dA.data_ptr(), dB.data_ptr(), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)))
+    return dX, dA, dB

@@ -1,0 +1,226 @@
+// capi.hip -- the C ABI of libqlora_nf4 (declared in include/qlora_nf4.h):
+// host-side validation, workspace layout and kernel launches.  Nothing here
+// allocates, frees or synchronises; every launch goes on the caller's stream.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/qlora_nf4.h"
+#include "common.h"
+
+using namespace qln;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return QL_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+int check_weight(const qlora_nf4_weight* w) {
+  if (!w) return fail(QL_ERR_NULL, "weight descriptor is NULL");
+  if (!w->codes || !w->qscale || !w->dscale) return fail(QL_ERR_NULL, "weight buffer is NULL");
+  if (w->block != 64 || w->dq_block != 256)
+    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (only 64 and 256)", w->block, w->dq_block);
+  if (w->rows <= 0 || w->cols <= 0 || w->cols % 64)
+    return fail(QL_ERR_SHAPE, "weight shape %lld x %lld (need positive, cols %% 64 == 0)",
+                (long long)w->rows, (long long)w->cols);
+  if (!aligned16(w->codes) || !aligned16(w->qscale) || !aligned16(w->dscale))
+    return fail(QL_ERR_ALIGN, "weight buffers must be 16-byte aligned");
+  return QL_OK;
+}
+
+NF4View view(const qlora_nf4_weight* w) {
+  NF4View v;
+  v.codes = w->codes;
+  v.qscale = w->qscale;
+  v.dscale = w->dscale;
+  v.N = w->rows;
+  v.K = w->cols;
+  return v;
+}
+
+int check_layer(const qlora_nf4_weight* w, int64_t M, int r, int compute_dtype) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (M <= 0) return fail(QL_ERR_SHAPE, "M=%lld must be positive", (long long)M);
+  if (r < 1 || r > QLORA_MAX_RANK) return fail(QL_ERR_UNSUPPORTED, "r=%d outside [1, %d]", r, QLORA_MAX_RANK);
+  if (compute_dtype != QL_DTYPE_BF16)
+    return fail(QL_ERR_UNSUPPORTED, "compute_dtype=%d (only QL_DTYPE_BF16)", compute_dtype);
+  if ((w->rows + 127) / 128 > kMaxGridY || (w->cols + 127) / 128 > kMaxGridY)
+    return fail(QL_ERR_SHAPE, "weight dimension too large");
+  if ((M + 127) / 128 > 0x7fffffffLL) return fail(QL_ERR_SHAPE, "M too large");
+  return QL_OK;
+}
+
+size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+  (void)N;
+  return align256((size_t)skinny_partial_elems(M, K, r) * sizeof(float));
+}
+
+// backward workspace: U fp32 [M][r] | T fp32 [M][r] (when recomputed) | fp32 split partials
+struct BwdLayout {
+  size_t u_off, t_off, part_off, total;
+};
+
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r) {
+  BwdLayout L;
+  const size_t mr = align256((size_t)M * (size_t)r * sizeof(float));
+  int64_t parts = std::max({skinny_partial_elems(M, N, r), skinny_partial_elems(N, M, r),
+                            skinny_partial_elems(K, M, r), skinny_partial_elems(M, K, r)});
+  L.u_off = 0;
+  L.t_off = mr;
+  L.part_off = 2 * mr;
+  L.total = L.part_off + align256((size_t)parts * sizeof(float));
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_abi_version(void) { return QLORA_ABI_VERSION; }
+
+const char* qlora_last_error(void) { return g_err.c_str(); }
+
+void nf4_levels(float out[16]) {
+  if (!out) return;
+  for (int i = 0; i < 16; ++i) std::memcpy(&out[i], &kNF4LevelBits[i], 4);
+}
+
+int nf4_storage_bytes(int64_t rows, int64_t cols, int block, int dq_block, size_t* codes_bytes,
+                      size_t* qscale_bytes, size_t* dscale_bytes) {
+  if (block != 64 || dq_block != 256)
+    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (only 64 and 256)", block, dq_block);
+  if (rows <= 0 || cols <= 0 || cols % 64)
+    return fail(QL_ERR_SHAPE, "shape %lld x %lld (need positive, cols %% 64 == 0)",
+                (long long)rows, (long long)cols);
+  const int64_t nb = rows * cols / 64;
+  if (codes_bytes) *codes_bytes = (size_t)(rows * cols / 2);
+  if (qscale_bytes) *qscale_bytes = (size_t)nb;
+  if (dscale_bytes) *dscale_bytes = (size_t)((nb + 255) / 256) * sizeof(float);
+  return ok();
+}
+
+int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
+                 uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out, void* stream) {
+  if (block != 64 || dq_block != 256)
+    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (only 64 and 256)", block, dq_block);
+  if (!W || !codes || !qscale || !dscale) return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (rows <= 0 || cols <= 0 || cols % 64)
+    return fail(QL_ERR_SHAPE, "shape %lld x %lld (need positive, cols %% 64 == 0)",
+                (long long)rows, (long long)cols);
+  if ((rows * cols / 64 + 255) / 256 > 0x7fffffffLL) return fail(QL_ERR_SHAPE, "weight too large");
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(qscale) || !aligned16(dscale) ||
+      (absmax_out && !aligned16(absmax_out)))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return hip_status(launch_quantize(W, rows, cols, codes, qscale, dscale, absmax_out,
+                                    (hipStream_t)stream),
+                    "nf4_quantize launch");
+}
+
+int nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (!W_bf16) return fail(QL_ERR_NULL, "output is NULL");
+  if (!aligned16(W_bf16)) return fail(QL_ERR_ALIGN, "output must be 16-byte aligned");
+  return hip_status(launch_dequantize(view(w), W_bf16, (hipStream_t)stream), "nf4_dequantize launch");
+}
+
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  return fwd_ws(M, N, K, r);
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int r, float alpha, int compute_dtype, uint16_t* Y,
+                     float* T_save, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layer(w, M, r, compute_dtype);
+  if (rc) return rc;
+  if (!X || !A || !B || !Y || !T_save) return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(T_save))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = fwd_ws(M, w->rows, w->cols, r);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (workspace && !aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const float s = alpha / (float)r;
+  hipError_t e = launch_lora_down(X, A, M, w->cols, r, (float*)workspace, T_save, st);
+  if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd: lora_down launch");
+  e = launch_fwd_main(view(w), X, M, T_save, B, r, s, Y, st);
+  return hip_status(e, "qlora_linear_fwd: main launch");
+}
+
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  return bwd_layout(M, N, K, r).total;
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha, int compute_dtype,
+                     const float* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layer(w, M, r, compute_dtype);
+  if (rc) return rc;
+  if (!X || !dY || !A || !B || !dA || !dB || !workspace)
+    return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+      !aligned16(dB) || !aligned16(workspace) || (T_saved && !aligned16(T_saved)) ||
+      (dX && !aligned16(dX)))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const int64_t N = w->rows, K = w->cols;
+  const BwdLayout L = bwd_layout(M, N, K, r);
+  if (workspace_bytes < L.total)
+    return fail(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* U = (float*)(ws + L.u_off);
+  float* part = (float*)(ws + L.part_off);
+  const float s = alpha / (float)r;
+  const float* T = T_saved;
+  hipError_t e;
+  if (!T) {
+    float* Tw = (float*)(ws + L.t_off);
+    e = launch_lora_down(X, A, M, K, r, part, Tw, st);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: T recompute launch");
+    T = Tw;
+  }
+  e = launch_lora_u(dY, B, M, N, r, part, U, st);
+  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: U launch");
+  e = launch_lora_db(dY, T, M, N, r, s, part, dB, st);
+  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dB launch");
+  if (dX) {
+    e = launch_dx_main(view(w), dY, M, U, A, r, s, dX, st);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dX launch");
+  }
+  e = launch_lora_da(U, X, M, K, r, s, part, dA, st);
+  return hip_status(e, "qlora_linear_bwd: dA launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// common.h -- internal declarations shared by the HIP sources of libqlora_nf4.
+//
+// Layout of a quantized weight W [N][K] (see include/qlora_nf4.h): codes are
+// row-major, two per byte (even element in the low nibble); block b covers
+// flattened elements [64b, 64b+64); group g covers blocks [256g, 256g+256).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qln {
+
+typedef uint16_t u16;
+
+// The 16 NF4 levels as fp32 bit patterns, code order.  Ultralytics glossary
+// "QLoRA", "How QLoRA works" (the level-building snippet): normal quantiles at
+// probabilities evenly spaced from 0.9677083 towards 0.5 (8 positive, 7
+// negative), an exact zero, sorted and divided by the largest; each value is
+// the exact formula rounded once to fp32.
+constexpr uint32_t kNF4LevelBits[16] = {
+    0xbf800000u, 0xbf3239b3u, 0xbf066b30u, 0xbeca32a0u,
+    0xbe91a24cu, 0xbe3d353fu, 0xbdba786bu, 0x00000000u,
+    0x3da2fb03u, 0x3e24cae1u, 0x3e7c04dcu, 0x3ead0338u,
+    0x3ee1a4b7u, 0x3f1007aau, 0x3f3913b1u, 0x3f800000u};
+
+struct NF4View {
+  const uint8_t* codes;
+  const uint8_t* qscale;
+  const float* dscale;
+  int64_t N, K;
+};
+
+// Decision points of the nearest-level rule: cut[j] is the smallest fp32 v
+// with fl32(L[j+1] - v) < fl32(v - L[j]), so the code of v in [-1, 1] is the
+// number of cut[j] <= v (ties go to the lower code, as argmin does).
+struct EncodeCuts {
+  float cut[15];
+};
+const EncodeCuts& encode_cuts();
+
+hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* qscale, float* dscale, float* absmax, hipStream_t s);
+hipError_t launch_dequantize(const NF4View& w, u16* out, hipStream_t s);
+
+// ---- GEMM family (gemm.hip) ----
+// Rank-side tile width for r (32, 64 or 128).
+int rank_tile(int r);
+
+struct SkinnyPlan {
+  int splits;          // contraction splits
+  int64_t c_per_split; // contraction length per split (multiple of 64)
+};
+// Split plan for an I x r output with contraction C.
+SkinnyPlan skinny_plan(int64_t I, int64_t C);
+
+// T = X A^T (fp32 partials in ws, summed into fp32 T) ; X [M][K], A [r][K]
+hipError_t launch_lora_down(const u16* X, const u16* A, int64_t M, int64_t K, int r,
+                            float* ws_partials, float* T, hipStream_t s);
+// U = dY B ; dY [M][N], B [N][r] -> U [M][r] fp32
+hipError_t launch_lora_u(const u16* dY, const u16* B, int64_t M, int64_t N, int r,
+                         float* ws_partials, float* U, hipStream_t s);
+// dB = s dY^T T ; -> dB [N][r] (T enters as hi + lo bf16)
+hipError_t launch_lora_db(const u16* dY, const float* T, int64_t M, int64_t N, int r, float s,
+                          float* ws_partials, u16* dB, hipStream_t st);
+// dA = s U^T X ; -> dA [r][K] (U enters as hi + lo bf16)
+hipError_t launch_lora_da(const float* U, const u16* X, int64_t M, int64_t K, int r, float s,
+                          float* ws_partials, u16* dA, hipStream_t st);
+// Y = X W'^T + s T B^T
+hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const float* T,
+                           const u16* B, int r, float s, u16* Y, hipStream_t st);
+// dX = dY W' + s U A
+hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const float* U,
+                          const u16* A, int r, float s, u16* dX, hipStream_t st);
+
+// Workspace (fp32 elements) the skinny partial sums of one call need.
+int64_t skinny_partial_elems(int64_t I, int64_t C, int r);
+
+}  // namespace qln

@@ -1,0 +1,178 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA NF4 linear layer.
+ *
+ * One frozen weight W [rows = N = out_features][cols = K = in_features] is
+ * stored as 4-bit NormalFloat codes with one absmax scale per block of 64
+ * consecutive weights of a row, and those block scales are themselves stored
+ * as 8-bit floats with one fp32 constant per group of 256 blocks.  The layer
+ * computes, for activations X [M][K] and LoRA adapters A [r][K], B [N][r]:
+ *
+ *   forward   Y  = X W'^T + s (X A^T) B^T,          s = alpha / r
+ *   backward  dX = dY W' + s (dY B) A
+ *             dA = s (dY B)^T X,   dB = s dY^T (X A^T)     (no gradient for W)
+ *
+ * where W' is the bfloat16 dequantized weight.  Sources (cited by page title
+ * and section):
+ *  - Ultralytics glossary "QLoRA", section "How QLoRA works": NF4 codes at
+ *    normal quantiles with one absmax scale per 64 weights; double
+ *    quantization of the scales to 8 bits in blocks of 256; the forward pass
+ *    dequantizes NF4 to bfloat16 right before the matrix product and adds the
+ *    LoRA path; the backward pass computes gradients through the dequantized
+ *    weights and updates only the two low-rank matrices.  Its closing note:
+ *    bnb_4bit_compute_dtype = bfloat16.
+ *  - vnread "Grokking QLoRA", section "Double Quantization": the second-level
+ *    format is FP8 (read here as OCP E4M3, largest scale of a group -> 448).
+ *  - Hugging Face Transformers docs "Bitsandbytes", section "QLoRA" (compute
+ *    data type, NF4, nested quantization) and the section on dequantizing a
+ *    model back to its original precision.
+ *  - IBM "What is LoRA?", PEFT parameters r and lora_alpha ("the scaling
+ *    factor"); ezsol "Mastering model fine-tuning", LoRA section: Delta W = B A.
+ *
+ * Conventions for every call:
+ *  - All tensors are dense row-major.  bf16 tensors are passed as uint16_t bit
+ *    patterns.  Pointers are DEVICE pointers unless stated otherwise; the
+ *    caller owns every buffer (the library never allocates, frees or
+ *    synchronises).  Work is enqueued on `stream` (a hipStream_t; NULL means
+ *    the null stream) and the call returns at once.
+ *  - Validation happens on the host before anything is enqueued: a failing
+ *    call enqueues nothing, returns a negative qlora_status and leaves a
+ *    message for qlora_last_error().  A launch failure reported by the HIP
+ *    runtime returns QL_ERR_HIP.  Faults inside a kernel surface at the
+ *    caller's next synchronisation.
+ *  - Preconditions that are documented, not checked: inputs are finite;
+ *    outputs do not overlap inputs or each other.
+ *  - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
+ *  - Stateless: concurrent calls on different streams are safe.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_ABI_VERSION 1
+
+typedef enum {
+  QL_OK = 0,
+  QL_ERR_NULL = -1,         /* a required pointer is NULL                          */
+  QL_ERR_SHAPE = -2,        /* a size is non-positive, or cols % 64 != 0           */
+  QL_ERR_UNSUPPORTED = -3,  /* block != 64, dq_block != 256, dtype != bf16, r range */
+  QL_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned             */
+  QL_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required          */
+  QL_ERR_HIP = -6           /* the HIP runtime reported an error at launch         */
+} qlora_status;
+
+enum { QL_DTYPE_BF16 = 1 };  /* the only compute dtype: bfloat16 operands, fp32 sums */
+
+#define QLORA_MAX_RANK 128
+
+/* A quantized frozen weight W [rows = N][cols = K] (device pointers).
+ *  codes  : N*K/2 bytes; byte e/2 holds flattened element e, even e in the low
+ *           nibble; the code indexes the 16 NF4 levels (nf4_levels()).
+ *  qscale : nb = N*K/64 bytes; OCP FP8 E4M3 code of each block's scale
+ *           (block b covers flattened elements [64b, 64b+64), always inside
+ *           one row because K % 64 == 0).
+ *  dscale : ng = ceil(nb/256) fp32; group g covers blocks [256g, 256g+256)
+ *           (the last group may be shorter); restored block scale is
+ *           fl32(E4M3(qscale[b]) * dscale[b/256]).
+ *  block, dq_block: must be 64 and 256. */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* qscale;
+  const float* dscale;
+  int64_t rows, cols;
+  int32_t block, dq_block;
+} qlora_nf4_weight;
+
+/* ABI version (QLORA_ABI_VERSION of the built library). */
+int qlora_abi_version(void);
+
+/* Message describing the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char* qlora_last_error(void);
+
+/* The 16 NF4 levels in code order (host memory, 16 floats).  Ultralytics
+ * "QLoRA", "How QLoRA works" (the level-building snippet): quantiles of the
+ * standard normal at probabilities evenly spaced from 0.9677083 towards 0.5 --
+ * 8 positive, 7 negative -- plus an exact zero, sorted and divided by the
+ * largest, each rounded once to fp32.  Code 0 is -1, code 7 is +0, code 15 is +1. */
+void nf4_levels(float out[16]);
+
+/* Storage of a quantized [rows][cols] weight (host outputs, any may be NULL):
+ * codes rows*cols/2 bytes, qscale rows*cols/64 bytes, dscale 4*ceil(nb/256)
+ * bytes.  Returns QL_OK or QL_ERR_SHAPE / QL_ERR_UNSUPPORTED. */
+int nf4_storage_bytes(int64_t rows, int64_t cols, int block, int dq_block,
+                      size_t* codes_bytes, size_t* qscale_bytes, size_t* dscale_bytes);
+
+/* Quantize an fp32 weight W [rows][cols] (device) to NF4 with double-quantized
+ * scales.  Ultralytics "QLoRA", "How QLoRA works" (NF4 and double
+ * quantization bullets, the encoding snippet):
+ *   a_b   = max |x| over block b (64 consecutive elements of a row)
+ *   code  = argmin_i fl32(|fl32(x / a_b) - L[i]|), lower code on a tie;
+ *           an all-zero block gets code 7 (the exact zero level)
+ *   d_g   = fl32(max_{b in g} a_b / 448)                       -> dscale[g]
+ *   q_b   = E4M3_RNE(fl32(a_b / d_g)), 0 when d_g == 0           -> qscale[b]
+ * Outputs: codes [rows*cols/2], qscale [nb], dscale [ng] (device);
+ * absmax_out [nb] fp32 (device, may be NULL) receives the exact a_b. */
+int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
+                 uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
+                 void* stream);
+
+/* Dequantize to bfloat16: W_bf16[e] = bf16_RNE(fl32(L[code_e] * s_b)) with the
+ * restored block scale s_b = fl32(E4M3(q_b) * d_g).  Transformers docs
+ * "Bitsandbytes", section on dequantizing a model to its original precision;
+ * Ultralytics "QLoRA" (restore = level times block scale).
+ * W_bf16: device, rows*cols uint16 (bf16 bits). */
+int nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, void* stream);
+
+/* Workspace the forward needs (bytes, 256-byte granular; may be 0). */
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+
+/* Forward of the QLoRA linear layer (Ultralytics "QLoRA", "How QLoRA works":
+ * dequantize to bf16 right before the matmul, then add the LoRA path).
+ *   T_save[m][j] = sum_k X[m][k] A[j][k]                     fp32 [M][r]
+ *   Y[m][n]      = bf16(sum_k X[m][k] W'[n][k] + s sum_j T[m][j] B[n][j])  [M][N]
+ * with s = fl32(alpha / r); products of bf16 operands summed in fp32 (MFMA);
+ * T enters the LoRA product as its bf16 rounding.  X [M][K], A [r][K],
+ * B [N][r] bf16 (device).  1 <= r <= QLORA_MAX_RANK.  compute_dtype must be
+ * QL_DTYPE_BF16.  T_save (fp32, required) is the saved activation the
+ * backward reuses; it is kept in fp32 because dB sums M products of it and
+ * a bf16 T would cost dB about 2^-9 * sqrt(M) of absolute accuracy.
+ * workspace: device, at least qlora_fwd_workspace_bytes(M, N, K, r) bytes
+ * (may be NULL when that is 0); its contents on return are unspecified. */
+int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha,
+                     int compute_dtype, uint16_t* Y, float* T_save,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace the backward needs (bytes, 256-byte granular). */
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+
+/* Backward of the QLoRA linear layer (Ultralytics "QLoRA", "How QLoRA works":
+ * gradients pass through the dequantized weights; only A and B receive
+ * gradients -- W stays frozen and gets none).  With U = dY B (fp32, kept in
+ * the workspace):
+ *   dX[m][k] = bf16(sum_n dY[m][n] W'[n][k] + s sum_j U[m][j] A[j][k])  [M][K]
+ *   dA[j][k] = bf16(s sum_m U[m][j] X[m][k])                           [r][K]
+ *   dB[n][j] = bf16(s sum_m dY[m][n] T[m][j])                          [N][r]
+ * U enters the dX product as its bf16 rounding; in dA and dB the fp32 U and
+ * T enter as a pair of bf16 terms (hi + lo), so those sums see them to about
+ * 2^-17 relative precision.
+ * T_saved: the forward's fp32 T_save, or NULL to recompute it in the workspace.
+ * dX may be NULL (skipped, e.g. for a first layer); dA and dB are required.
+ * Outputs are overwritten, never accumulated into.  W's buffers are only
+ * read.  workspace: device, >= qlora_bwd_workspace_bytes(M, N, K, r). */
+int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
+                     int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                     int compute_dtype, const float* T_saved,
+                     uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_NF4_H */

@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_qlora_bwd_dx.restype = I
         L.oracle_qlora_bwd_adapters.argtypes = [I64, I64, P, P, I64, P, P, I, D, P, P, I]
         L.oracle_qlora_bwd_adapters.restype = I
+        L.oracle_qlora_adapter_entries.argtypes = [I64, I64, P, P, I64, P, P, I, D, I64, P, P, P,
+                                                   I64, P, P, P, I]
+        L.oracle_qlora_adapter_entries.restype = I
         _lib = L
     return _lib
 
@@ -204,3 +207,23 @@ def qlora_bwd_adapters(X, dY, A, B, alpha: float, want_dA=True, want_dB=True,
                                            _ptr(dA), _ptr(dB), threads or default_threads()),
            "qlora_bwd_adapters")
     return dA, dB
+
+
+def qlora_adapter_entries(X, dY, A, B, alpha: float, dA_idx, dB_idx, threads: int | None = None):
+    """Selected entries: dA at (j, k) pairs, dB at (n, j) pairs (double)."""
+    X, dY, A, B = _u16(X), _u16(dY), _u16(A), _u16(B)
+    M, K = X.shape
+    N = dY.shape[1]
+    r = A.shape[0]
+    ia = np.ascontiguousarray(np.asarray(dA_idx, np.int64).reshape(-1, 2))
+    ib = np.ascontiguousarray(np.asarray(dB_idx, np.int64).reshape(-1, 2))
+    aj, ak = np.ascontiguousarray(ia[:, 0]), np.ascontiguousarray(ia[:, 1])
+    bn, bj = np.ascontiguousarray(ib[:, 0]), np.ascontiguousarray(ib[:, 1])
+    oa = np.zeros(len(ia), np.float64)
+    ob = np.zeros(len(ib), np.float64)
+    _check(lib().oracle_qlora_adapter_entries(N, K, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r,
+                                              alpha, len(ia), _ptr(aj), _ptr(ak), _ptr(oa),
+                                              len(ib), _ptr(bn), _ptr(bj), _ptr(ob),
+                                              threads or default_threads()),
+           "qlora_adapter_entries")
+    return oa, ob

@@ -439,3 +439,72 @@ int oracle_qlora_bwd_adapters(int64_t N, int64_t K, const uint16_t* X, const uin
   free(U);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Selected dA / dB entries.  Same definitions as above: columns of U and T  */
+/* in double for the ranks the entries use, then one sum over m per entry.   */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t N, K, M; const uint16_t* X; const uint16_t* dY; const uint16_t* A; const uint16_t* B;
+  int r; const int* need_u; const int* need_t; double* Ucol; double* Tcol;
+} col_ctx;
+
+static void col_range(void* p, int64_t m0, int64_t m1) {
+  col_ctx* c = (col_ctx*)p;
+  for (int64_t m = m0; m < m1; ++m) {
+    for (int j = 0; j < c->r; ++j) {
+      if (c->need_u[j]) {
+        double u = 0.0;
+        for (int64_t n = 0; n < c->N; ++n)
+          u += bf16_to_double(c->dY[m * c->N + n]) * bf16_to_double(c->B[n * c->r + j]);
+        c->Ucol[(int64_t)j * c->M + m] = u;
+      }
+      if (c->need_t[j]) {
+        double t = 0.0;
+        for (int64_t k = 0; k < c->K; ++k)
+          t += bf16_to_double(c->X[m * c->K + k]) * bf16_to_double(c->A[(int64_t)j * c->K + k]);
+        c->Tcol[(int64_t)j * c->M + m] = t;
+      }
+    }
+  }
+}
+
+int oracle_qlora_adapter_entries(int64_t N, int64_t K, const uint16_t* X, const uint16_t* dY,
+                                 int64_t M, const uint16_t* A, const uint16_t* B, int r,
+                                 double alpha, int64_t n_dA, const int64_t* dA_j,
+                                 const int64_t* dA_k, double* dA_out, int64_t n_dB,
+                                 const int64_t* dB_n, const int64_t* dB_j, double* dB_out,
+                                 int nthreads) {
+  if (!X || !dY || !A || !B || N <= 0 || K <= 0 || M <= 0 || r <= 0) return -1;
+  int* need_u = (int*)calloc((size_t)r, sizeof(int));
+  int* need_t = (int*)calloc((size_t)r, sizeof(int));
+  if (!need_u || !need_t) { free(need_u); free(need_t); return -1; }
+  for (int64_t i = 0; i < n_dA; ++i) {
+    if (dA_j[i] < 0 || dA_j[i] >= r || dA_k[i] < 0 || dA_k[i] >= K) { free(need_u); free(need_t); return -2; }
+    need_u[dA_j[i]] = 1;
+  }
+  for (int64_t i = 0; i < n_dB; ++i) {
+    if (dB_j[i] < 0 || dB_j[i] >= r || dB_n[i] < 0 || dB_n[i] >= N) { free(need_u); free(need_t); return -2; }
+    need_t[dB_j[i]] = 1;
+  }
+  double* Ucol = (double*)malloc((size_t)(M * r) * sizeof(double));
+  double* Tcol = (double*)malloc((size_t)(M * r) * sizeof(double));
+  if (!Ucol || !Tcol) { free(Ucol); free(Tcol); free(need_u); free(need_t); return -1; }
+  col_ctx cc = { N, K, M, X, dY, A, B, r, need_u, need_t, Ucol, Tcol };
+  parallel_for(M, nthreads, col_range, &cc);
+  const double s = alpha / (double)r;
+  for (int64_t i = 0; i < n_dA; ++i) {
+    double acc = 0.0;
+    for (int64_t m = 0; m < M; ++m)
+      acc += Ucol[dA_j[i] * M + m] * bf16_to_double(X[m * K + dA_k[i]]);
+    dA_out[i] = s * acc;
+  }
+  for (int64_t i = 0; i < n_dB; ++i) {
+    double acc = 0.0;
+    for (int64_t m = 0; m < M; ++m)
+      acc += bf16_to_double(dY[m * N + dB_n[i]]) * Tcol[dB_j[i] * M + m];
+    dB_out[i] = s * acc;
+  }
+  free(Ucol); free(Tcol); free(need_u); free(need_t);
+  return 0;
+}

@@ -100,6 +100,17 @@ int oracle_qlora_bwd_adapters(int64_t N, int64_t K, const uint16_t* X, const uin
                               int64_t M, const uint16_t* A, const uint16_t* B, int r,
                               double alpha, double* dA_out, double* dB_out, int nthreads);
 
+/* Selected entries of dA and dB (for shapes too large to compute in full):
+ * dA[dA_j[i], dA_k[i]] -> dA_out[i] and dB[dB_n[i], dB_j[i]] -> dB_out[i], with
+ * the same definitions as oracle_qlora_bwd_adapters.  Columns of U = dY B and
+ * T = X A^T are computed in double for the ranks the entries touch. */
+int oracle_qlora_adapter_entries(int64_t N, int64_t K, const uint16_t* X, const uint16_t* dY,
+                                 int64_t M, const uint16_t* A, const uint16_t* B, int r,
+                                 double alpha, int64_t n_dA, const int64_t* dA_j,
+                                 const int64_t* dA_k, double* dA_out, int64_t n_dB,
+                                 const int64_t* dB_n, const int64_t* dB_j, double* dB_out,
+                                 int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

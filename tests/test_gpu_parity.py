@@ -1,0 +1,235 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Bit-exact: NF4 codes, E4M3 scale bytes, group constants, exact block absmax
+and dequantized bf16 weights.  Within the fp bar (tests/helpers.py): Y, T,
+dX, dA, dB.  Small shapes are checked in full; the five workload shapes at
+their real sizes are checked on sampled rows / entries, with quantize and
+dequantize still compared in full."""
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from helpers import GpuLayer, assert_close, bf16_tensor, log, tensor_bits, tensor_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_nf4_quantized_17_amd as q  # noqa: E402
+
+
+def _quant_host(w):
+    return (w.codes.cpu().numpy(), w.qscale.cpu().numpy(), w.dscale.cpu().numpy())
+
+
+def check_quantize(orc, W: np.ndarray, label: str):
+    log(f"[quantize] {label} shape={W.shape}")
+    dW = torch.from_numpy(np.ascontiguousarray(W)).cuda()
+    absmax = torch.empty(W.size // 64, dtype=torch.float32, device="cuda")
+    w = q.nf4_quantize(dW, absmax=absmax)
+    codes, qs, ds = _quant_host(w)
+    rc, rq, rd, ra = orc.nf4_quantize(W)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), label
+    bad = np.nonzero(codes != rc)[0]
+    assert bad.size == 0, f"{label}: {bad.size} code bytes differ, first at {bad[:5]}"
+    assert np.array_equal(qs, rq), f"{label}: qscale differs"
+    assert np.array_equal(ds.view(np.uint32), rd.view(np.uint32)), f"{label}: dscale differs"
+    log(f"[dequantize] {label}")
+    deq = tensor_bits(q.nf4_dequantize(w))
+    ref = orc.nf4_dequantize(rc, rq, rd, *W.shape)
+    assert np.array_equal(deq, ref), f"{label}: dequantized bf16 differs"
+    return w, ref
+
+
+# ---------------------------------------------------------------------------
+# quantize / dequantize: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,outliers", [(256, 256, 0.0), (64, 192, 0.0), (300, 256, 0.01),
+                                          (7, 320, 0.0), (1, 64, 0.0), (513, 1088, 0.01)])
+def test_quantize_bitwise_shapes(orc, N, K, outliers):
+    cfg = si.custom(N=N, K=K, M=1, r=8, outlier_frac=outliers, seed=N + K)
+    check_quantize(orc, si.weight(cfg, 0), f"{N}x{K}")
+
+
+def _edge_weight(orc):
+    """Blocks that exercise every corner of the encoder: all-zero, exact ties,
+    decision points and their fp32 neighbours, subnormal and huge scales,
+    elements tiny against their scale, negative absmax, a lone nonzero."""
+    L = orc.nf4_levels()
+    rng = np.random.default_rng(99)
+    blocks = []
+    blocks.append(np.zeros(64, np.float32))
+    ties = np.array([int(x, 16) for x in ("beeb8480", "beadea76", "bd3a786b", "3d22fb03",
+                                           "3e9582d3")], np.uint32).view(np.float32)
+    b = np.zeros(64, np.float32); b[0] = -1.0; b[1:6] = ties; b[6:11] = -ties
+    blocks.append(b)
+    mids = []
+    for j in range(15):
+        m = np.float32((float(L[j]) + float(L[j + 1])) / 2)
+        for d in range(-3, 4):
+            mids.append(np.float32(m + np.float32(d) * np.spacing(m)))
+    mids = np.array(mids, np.float32)
+    for i in range(0, mids.size, 63):
+        b = np.zeros(64, np.float32); b[0] = 1.0
+        chunk = mids[i:i + 63]
+        b[1:1 + chunk.size] = chunk
+        blocks.append(b)
+    for sc in (1e-40, 3e-39, 1e-35, 1e-30, 7e25, 1e35, 1e37):
+        b = (rng.standard_normal(64).astype(np.float32) * np.float32(sc)).astype(np.float32)
+        blocks.append(b)
+    b = np.full(64, 1e-30, np.float32); b[5] = 1.0; b[7] = -3e-42
+    blocks.append(b)
+    b = rng.standard_normal(64).astype(np.float32); b[13] = -10.0
+    blocks.append(b)
+    b = np.zeros(64, np.float32); b[40] = -2.5e-3
+    blocks.append(b)
+    for _ in range(3):
+        blocks.append((rng.standard_normal(64) * 0.02).astype(np.float32))
+    n = len(blocks)
+    pad = (-n) % 4
+    blocks += [np.zeros(64, np.float32)] * pad
+    return np.concatenate(blocks).reshape(-1, 256)
+
+
+def test_quantize_bitwise_edge_blocks(orc):
+    W = _edge_weight(orc)
+    check_quantize(orc, W, "edge blocks")
+
+
+def test_quantize_bitwise_group_of_zero_blocks(orc):
+    W = np.zeros((64, 512), np.float32)        # 512 zero blocks: two groups with d = 0
+    W[40, 100] = 1e-3                          # one nonzero in the second group
+    check_quantize(orc, W, "mostly zero")
+
+
+# ---------------------------------------------------------------------------
+# forward / backward: fp bar, full outputs on small shapes
+# ---------------------------------------------------------------------------
+SMALL = [
+    # N, K, M, r, alpha
+    (256, 256, 16, 8, 16.0),      # the tiny workload
+    (100, 192, 5, 3, 6.0),        # N and r not multiples of 8
+    (130, 320, 129, 17, 34.0),    # ragged tiles in every dimension
+    (64, 64, 1, 1, 2.0),
+    (200, 128, 300, 128, 16.0),   # maximum rank
+    (384, 512, 257, 64, 16.0),
+]
+
+
+@pytest.mark.parametrize("N,K,M,r,alpha", SMALL)
+def test_fwd_bwd_small(orc, N, K, M, r, alpha):
+    cfg = si.custom(N=N, K=K, M=M, r=r, alpha=alpha, seed=7 * N + K)
+    lay = GpuLayer(cfg)
+    log(f"[fwd] N={N} K={K} M={M} r={r}")
+    Y, T = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, lay.dB_in, alpha)
+    torch.cuda.synchronize()
+    codes, qs, ds = _quant_host(lay.w)
+    Wdq = orc.nf4_dequantize(codes, qs, ds, N, K)
+    Yr, Tr = orc.qlora_fwd(Wdq, lay.X, lay.A, lay.B, alpha)
+    assert_close(tensor_f64(T), Tr, "T")
+    assert_close(tensor_f64(Y), Yr, "Y")
+    log(f"[bwd] N={N} K={K} M={M} r={r}")
+    dX, dA, dB = q.qlora_linear_bwd(lay.w, lay.dX_in, lay.ddY, lay.dA_in, lay.dB_in, alpha, T=T)
+    torch.cuda.synchronize()
+    dXr = orc.qlora_bwd_dx(Wdq, lay.dY, lay.A, lay.B, alpha)
+    dAr, dBr = orc.qlora_bwd_adapters(lay.X, lay.dY, lay.A, lay.B, alpha)
+    assert_close(tensor_f64(dX), dXr, "dX")
+    assert_close(tensor_f64(dA), dAr, "dA")
+    assert_close(tensor_f64(dB), dBr, "dB")
+
+
+def test_zero_B_gives_bitwise_base_output(orc):
+    cfg = si.custom(N=384, K=512, M=100, r=16, alpha=32.0, seed=3)
+    lay = GpuLayer(cfg)
+    log("[fwd] zero-B invariant")
+    Bz = torch.zeros_like(lay.dB_in)
+    Y0, _ = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, Bz, 32.0)
+    Ya, _ = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, lay.dB_in, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.float(), Ya.float())
+    codes, qs, ds = _quant_host(lay.w)
+    Wdq = orc.nf4_dequantize(codes, qs, ds, lay.N, lay.K)
+    Yr, _ = orc.qlora_fwd(Wdq, lay.X, lay.A, lay.B, 0.0)
+    assert_close(tensor_f64(Y0), Yr, "Y base")
+    log("[bwd] zero-B: dA must be exactly zero")
+    _, dA, _ = q.qlora_linear_bwd(lay.w, lay.dX_in, lay.ddY, lay.dA_in, Bz, 32.0, want_dX=False)
+    torch.cuda.synchronize()
+    assert float(dA.float().abs().max()) == 0.0
+
+
+def test_bwd_variants_agree_and_are_deterministic(orc):
+    cfg = si.custom(N=320, K=256, M=200, r=24, alpha=16.0, seed=5)
+    lay = GpuLayer(cfg)
+    before = [t.clone() for t in (lay.w.codes, lay.w.qscale, lay.w.dscale)]
+    log("[bwd] variants")
+    _, T = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, lay.dB_in, 16.0)
+    r1 = q.qlora_linear_bwd(lay.w, lay.dX_in, lay.ddY, lay.dA_in, lay.dB_in, 16.0, T=T)
+    r2 = q.qlora_linear_bwd(lay.w, lay.dX_in, lay.ddY, lay.dA_in, lay.dB_in, 16.0, T=T)
+    r3 = q.qlora_linear_bwd(lay.w, lay.dX_in, lay.ddY, lay.dA_in, lay.dB_in, 16.0, T=None)
+    r4 = q.qlora_linear_bwd(lay.w, lay.dX_in, lay.ddY, lay.dA_in, lay.dB_in, 16.0, T=T,
+                            want_dX=False)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run"
+    for a, b in zip(r1, r3):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "T recomputed"
+    assert r4[0] is None
+    for a, b in zip(r1[1:], r4[1:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "dX skipped"
+    for a, b in zip(before, (lay.w.codes, lay.w.qscale, lay.w.dscale)):
+        assert torch.equal(a, b), "the frozen weight was written"
+
+
+# ---------------------------------------------------------------------------
+# the five workload shapes at their real sizes
+# ---------------------------------------------------------------------------
+def _sample_rows(M, k=5, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    rows.update(int(x) for x in rng.integers(0, M, k))
+    return sorted(rows)
+
+
+def _check_layer_full_size(orc, cfg, li, M=None, bwd=True):
+    lay = GpuLayer(cfg, li, M=M, quantize=False)
+    label = f"{cfg.key}/{cfg.layers[li].name} M={lay.M}"
+    w, Wdq = check_quantize(orc, lay.W, label)
+    lay.w = w
+    log(f"[fwd] {label}")
+    Y, T = q.qlora_linear_fwd(w, lay.dX_in, lay.dA_in, lay.dB_in, lay.alpha)
+    torch.cuda.synchronize()
+    rows = _sample_rows(lay.M, seed=li)
+    Yr, Tr = orc.qlora_fwd(Wdq, lay.X, lay.A, lay.B, lay.alpha, rows=rows)
+    assert_close(tensor_f64(Y[rows]), Yr, f"{label} Y rows")
+    assert_close(tensor_f64(T[rows]), Tr, f"{label} T rows")
+    if not bwd:
+        return
+    log(f"[bwd] {label}")
+    dX, dA, dB = q.qlora_linear_bwd(w, lay.dX_in, lay.ddY, lay.dA_in, lay.dB_in, lay.alpha, T=T)
+    torch.cuda.synchronize()
+    dXr = orc.qlora_bwd_dx(Wdq, lay.dY, lay.A, lay.B, lay.alpha, rows=rows)
+    assert_close(tensor_f64(dX[rows]), dXr, f"{label} dX rows")
+    rng = np.random.default_rng(li + 11)
+    ia = [(int(j), int(k)) for j, k in zip(rng.integers(0, lay.r, 24), rng.integers(0, lay.K, 24))]
+    ib = [(int(n), int(j)) for n, j in zip(rng.integers(0, lay.N, 24), rng.integers(0, lay.r, 24))]
+    ia += [(0, 0), (lay.r - 1, lay.K - 1)]
+    ib += [(0, 0), (lay.N - 1, lay.r - 1)]
+    ea, eb = orc.qlora_adapter_entries(lay.X, lay.dY, lay.A, lay.B, lay.alpha, ia, ib)
+    ga = tensor_f64(dA)
+    gb = tensor_f64(dB)
+    assert_close(np.array([ga[j, k] for j, k in ia]), ea, f"{label} dA entries")
+    assert_close(np.array([gb[n, j] for n, j in ib]), eb, f"{label} dB entries")
+
+
+@pytest.mark.parametrize("key,li", [("c1", 0), ("c2", 0), ("c3", 0), ("c3", 2), ("c4", 0),
+                                    ("c4", 1)])
+def test_workload_shapes(orc, key, li):
+    _check_layer_full_size(orc, si.CONFIGS[key], li)
+
+
+@pytest.mark.parametrize("li", [0, 1])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_shapes(orc, li, M):
+    _check_layer_full_size(orc, si.CONFIGS["c5"], li, M=M, bwd=False)

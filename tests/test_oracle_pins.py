@@ -405,3 +405,13 @@ def test_results_do_not_depend_on_thread_count(orc):
     y1, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha, threads=1)
     y3, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha, threads=3)
     assert np.array_equal(y1, y3)
+
+
+def test_adapter_entries_match_full_adapters(orc):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc, N=40, K=128, M=9, r=5)
+    dA, dB = orc.qlora_bwd_adapters(X, dY, A, B, cfg.alpha)
+    ia = [(0, 3), (4, 127), (2, 64), (4, 0)]
+    ib = [(39, 4), (0, 0), (17, 2)]
+    ea, eb = orc.qlora_adapter_entries(X, dY, A, B, cfg.alpha, ia, ib)
+    assert np.array_equal(ea, np.array([dA[j, k] for j, k in ia]))
+    assert np.array_equal(eb, np.array([dB[n, j] for n, j in ib]))
