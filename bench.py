@@ -1,0 +1,407 @@
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input,
+on the 70B-class MLP slice (W 28672x8192 "up" and 8192x28672 "down", 4096
+tokens, LoRA rank 64, alpha 16; weights N(0, 0.02) with 1% x20 outliers):
+    nf4_quantize(up), nf4_quantize(down)          absmax, encode, pack, double quant
+    qlora_linear_fwd(up), qlora_linear_fwd(down)  T = X A^T, fused dequant GEMM + LoRA
+    qlora_linear_bwd(down), qlora_linear_bwd(up)  U, dB, fused dequant dX GEMM, dA
+    qlora_linear_fwd(up|down) at M = 16           the decode-sized forward
+Inputs are resident in HBM before timing starts.  value = algorithmic flops
+of the step (4MNK + 6Mr(N+K) per trained linear, plus the decode forwards;
+dequantization and quantization count no flops) / wall time of the step.
+
+Also reported: the roofline of the dominant kernel (HIP events recorded by
+the library's timing hook around that kernel's launches), the decode-shape
+and quantize bandwidths against HBM, and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s (bf16 MFMA) and NF4 decode GB/s vs roofline"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HIP events straight from the runtime (the library records them on the
+# stream its kernels are launched on)
+# ---------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        # resolve through libqlora_nf4's handle: the HIP runtime already loaded
+        # in this process (the one torch and the library use), never a second copy
+        import bit_nf4_quantized_17_amd as q
+        self.L = q.lib()
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, ev, stream):
+        assert self.L.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.L.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+# ---------------------------------------------------------------------------
+# workload
+# ---------------------------------------------------------------------------
+def linear_flops(M, N, K, r):
+    """fwd 2MNK + 2Mr(K+N); bwd 2MNK + 4Mr(K+N) (dX base, U, U A, dA, dB)."""
+    fwd = 2 * M * N * K + 2 * M * r * (K + N)
+    bwd = 2 * M * N * K + 4 * M * r * (K + N)
+    return fwd, bwd
+
+
+def decode_bytes(M, N, K, r):
+    """Algorithmic bytes of one decode-sized forward: the NF4 weight (codes,
+    E4M3 scales, group constants), X, Y, A, B and the fp32 T."""
+    nb = N * K // 64
+    w = N * K // 2 + nb + 4 * ((nb + 255) // 256)
+    return w + 2 * M * K + 2 * M * N + 2 * r * K + 2 * N * r + 4 * M * r
+
+
+def quantize_bytes(N, K):
+    """fp32 read + packed codes + E4M3 scales + group constants written."""
+    nb = N * K // 64
+    return 4 * N * K + N * K // 2 + nb + 4 * ((nb + 255) // 256)
+
+
+class Layer:
+    def __init__(self, cfg, li, M_decode=16):
+        import torch
+        import bit_nf4_quantized_17_amd as q
+        import synthetic_inputs as si
+        from tests.helpers import bf16_tensor
+        L = cfg.layers[li]
+        self.name, self.N, self.K, self.M, self.r, self.alpha = L.name, L.N, L.K, cfg.M, cfg.r, cfg.alpha
+        self.W = torch.from_numpy(si.weight(cfg, li)).cuda()
+        self.X = bf16_tensor(si.activations(cfg, li))
+        A, B = si.adapters(cfg, li)
+        self.A, self.B = bf16_tensor(A), bf16_tensor(B)
+        self.dY = bf16_tensor(si.upstream(cfg, li))
+        self.w = q.NF4Weight.empty(self.N, self.K)
+        dev = "cuda"
+        self.Y = torch.empty(self.M, self.N, dtype=torch.bfloat16, device=dev)
+        self.T = torch.empty(self.M, self.r, dtype=torch.float32, device=dev)
+        self.dXo = torch.empty(self.M, self.K, dtype=torch.bfloat16, device=dev)
+        self.dA = torch.empty(self.r, self.K, dtype=torch.bfloat16, device=dev)
+        self.dB = torch.empty(self.N, self.r, dtype=torch.bfloat16, device=dev)
+        self.wsf = torch.empty(max(256, q.qlora_fwd_workspace_bytes(self.M, self.N, self.K, self.r)),
+                               dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(q.qlora_bwd_workspace_bytes(self.M, self.N, self.K, self.r),
+                               dtype=torch.uint8, device=dev)
+        self.Md = M_decode
+        self.Xd = self.X[:M_decode].contiguous()
+        self.Yd = torch.empty(M_decode, self.N, dtype=torch.bfloat16, device=dev)
+        self.Td = torch.empty(M_decode, self.r, dtype=torch.float32, device=dev)
+        self.wsd = torch.empty(max(256, q.qlora_fwd_workspace_bytes(M_decode, self.N, self.K, self.r)),
+                               dtype=torch.uint8, device=dev)
+
+    def quantize(self):
+        import bit_nf4_quantized_17_amd as q
+        q.nf4_quantize(self.W, out=self.w)
+
+    def fwd(self):
+        import bit_nf4_quantized_17_amd as q
+        q.qlora_linear_fwd(self.w, self.X, self.A, self.B, self.alpha, Y=self.Y, T=self.T,
+                           workspace=self.wsf)
+
+    def bwd(self):
+        import bit_nf4_quantized_17_amd as q
+        q.qlora_linear_bwd(self.w, self.X, self.dY, self.A, self.B, self.alpha, T=self.T,
+                           dX=self.dXo, dA=self.dA, dB=self.dB, workspace=self.wsb)
+
+    def decode(self):
+        import bit_nf4_quantized_17_amd as q
+        q.qlora_linear_fwd(self.w, self.Xd, self.A, self.B, self.alpha, Y=self.Yd, T=self.Td,
+                           workspace=self.wsd)
+
+    def flops(self):
+        f, b = linear_flops(self.M, self.N, self.K, self.r)
+        d, _ = linear_flops(self.Md, self.N, self.K, self.r)
+        return f, b, d
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_nf4_quantized_17_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, src_hash: str):
+    """Per-launch HBM bytes measured with rocprofv3 counters (profiles/), or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path)).get(kernel_key)
+    except (ValueError, OSError):
+        return None
+    if not d or d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# decode and quantize bandwidth (cache-defeating rotation over >= 512 MB)
+# ---------------------------------------------------------------------------
+def bench_decode(hip, reps=60):
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    import synthetic_inputs as si
+    from tests.helpers import bf16_tensor
+    cfg = si.CONFIGS["c5"]
+    out = []
+    st = torch.cuda.current_stream().cuda_stream
+    for li, L in enumerate(cfg.layers):
+        w0 = q.nf4_quantize(torch.from_numpy(si.weight(cfg, li)).cuda())
+        wbytes = sum(t.numel() * t.element_size() for t in (w0.codes, w0.qscale, w0.dscale))
+        ncopy = max(2, -(-512 * 2**20 // wbytes))
+        copies = [w0] + [q.NF4Weight(w0.codes.clone(), w0.qscale.clone(), w0.dscale.clone(),
+                                     w0.rows, w0.cols) for _ in range(ncopy - 1)]
+        A, B = si.adapters(cfg, li)
+        A, B = bf16_tensor(A), bf16_tensor(B)
+        for M in cfg.decode_M:
+            X = bf16_tensor(si.activations(cfg, li, M))
+            Y = torch.empty(M, L.N, dtype=torch.bfloat16, device="cuda")
+            T = torch.empty(M, cfg.r, dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(256, q.qlora_fwd_workspace_bytes(M, L.N, L.K, cfg.r)),
+                             dtype=torch.uint8, device="cuda")
+            for i in range(5):
+                q.qlora_linear_fwd(copies[i % ncopy], X, A, B, cfg.alpha, Y=Y, T=T, workspace=ws)
+            e0, e1 = hip.event(), hip.event()
+            torch.cuda.synchronize()
+            hip.record(e0, st)
+            for i in range(reps):
+                q.qlora_linear_fwd(copies[i % ncopy], X, A, B, cfg.alpha, Y=Y, T=T, workspace=ws)
+            hip.record(e1, st)
+            ms = hip.elapsed_ms(e0, e1) / reps
+            gbs = decode_bytes(M, L.N, L.K, cfg.r) / (ms * 1e-3) / 1e9
+            out.append({"W": f"{L.N}x{L.K}", "M": M, "us_per_call": round(ms * 1e3, 2),
+                        "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        del copies, w0
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_quantize(hip, layers, reps=20):
+    import torch
+    st = torch.cuda.current_stream().cuda_stream
+    res = []
+    for lay in layers:
+        e0, e1 = hip.event(), hip.event()
+        lay.quantize()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for _ in range(reps):
+            lay.quantize()
+        hip.record(e1, st)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        gbs = quantize_bytes(lay.N, lay.K) / (ms * 1e-3) / 1e9
+        res.append({"W": f"{lay.N}x{lay.K}", "us_per_call": round(ms * 1e3, 1),
+                    "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(lay, target_s=15.0):
+    import numpy as np
+    import oracle
+    from tests.helpers import tensor_bits
+    threads = oracle.default_threads()
+    codes = lay.w.codes.cpu().numpy()
+    qs = lay.w.qscale.cpu().numpy()
+    ds = lay.w.dscale.cpu().numpy()
+    Wdq = oracle.nf4_dequantize(codes, qs, ds, lay.N, lay.K)
+    X, A, B, dY = (tensor_bits(t) for t in (lay.X, lay.A, lay.B, lay.dY))
+    row_flops = (2 * lay.N * lay.K + 2 * lay.r * (lay.K + lay.N)) + \
+        (2 * lay.N * lay.K + 2 * lay.r * (lay.K + lay.N))
+
+    def run(nrows):
+        rows = np.arange(nrows, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.qlora_fwd(Wdq, X, A, B, lay.alpha, rows=rows, threads=threads)
+        oracle.qlora_bwd_dx(Wdq, dY, A, B, lay.alpha, rows=rows, threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(threads)                      # calibration: one row per thread
+    n = int(max(threads, min(lay.M, threads * max(1, round(target_s / max(t1, 1e-3))))))
+    n = (n // threads) * threads
+    t = run(n)
+    tf = n * row_flops / t / 1e12
+    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 2),
+            "sample": f"{n} token rows of the {lay.name} projection ({lay.N}x{lay.K}, r={lay.r}): "
+                      f"forward rows of Y (with T) and backward rows of dX (with U), double sums"}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip decode/quantize bandwidth runs")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    import synthetic_inputs as si
+
+    torch.cuda.set_device(0)
+    hip = Hip()
+    cfg = si.CONFIGS["c4"]
+    log("[bench] generating the 70B-class MLP slice inputs")
+    layers = [Layer(cfg, 0), Layer(cfg, 1)]
+    up, down = layers
+
+    def step():
+        up.quantize()
+        down.quantize()
+        up.fwd()
+        down.fwd()
+        down.bwd()
+        up.bwd()
+        up.decode()
+        down.decode()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel events through the library's hook
+    st = torch.cuda.current_stream().cuda_stream
+    K = args.steps
+    ev = {k: [[hip.event(), hip.event()] for _ in range(K)] for k in ("fwd_up", "fwd_down",
+                                                                     "dx_up", "dx_down")}
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        up.quantize()
+        down.quantize()
+        q.qlora_set_timing_events(ev["fwd_up"][s][0], ev["fwd_up"][s][1])
+        up.fwd()
+        q.qlora_set_timing_events(ev["fwd_down"][s][0], ev["fwd_down"][s][1])
+        down.fwd()
+        q.qlora_set_timing_events(None, None, ev["dx_down"][s][0], ev["dx_down"][s][1])
+        down.bwd()
+        q.qlora_set_timing_events(None, None, ev["dx_up"][s][0], ev["dx_up"][s][1])
+        up.bwd()
+        q.qlora_set_timing_events()
+        up.decode()
+        down.decode()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+
+    kern = {k: sum(hip.elapsed_ms(a, b) for a, b in v) / K for k, v in ev.items()}
+    step_flops = sum(sum(l.flops()) for l in layers)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    # the dominant kernel: the larger of the fused fwd GEMM and the fused dX GEMM
+    fwd_ms = (kern["fwd_up"] + kern["fwd_down"]) / 2
+    dx_ms = (kern["dx_up"] + kern["dx_down"]) / 2
+    main_flops = 2 * cfg.M * up.N * up.K + 2 * cfg.M * up.N * cfg.r   # base + LoRA prologue
+    if dx_ms >= fwd_ms:
+        dom, dom_ms = "k_gemm dX (NF4 transposed producer, U A prologue)", dx_ms
+        dom_key = "gemm_dx"
+    else:
+        dom, dom_ms = "k_gemm fwd (NF4 producer, T B^T prologue)", fwd_ms
+        dom_key = "gemm_fwd"
+    achieved = main_flops / (dom_ms * 1e-3) / 1e12
+    src = source_hash("gemm.hip")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(dom_key, src), "kernel": dom,
+                "launch_ms": round(dom_ms, 4), "flops_per_launch": main_flops,
+                "other_gemm_ms": round(min(dx_ms, fwd_ms), 4)}
+
+    # per-call breakdown (one extra step with events around every call)
+    calls = [("quantize_up", up.quantize), ("quantize_down", down.quantize), ("fwd_up", up.fwd),
+             ("fwd_down", down.fwd), ("bwd_down", down.bwd), ("bwd_up", up.bwd),
+             ("decode_up_M16", up.decode), ("decode_down_M16", down.decode)]
+    ce = [(n, f, hip.event(), hip.event()) for n, f in calls]
+    torch.cuda.synchronize()
+    for n, f, a, b in ce:
+        hip.record(a, st)
+        f()
+        hip.record(b, st)
+    breakdown = {n: round(hip.elapsed_ms(a, b), 4) for n, f, a, b in ce}
+    fb_ms = sum(breakdown[k] for k in ("fwd_up", "fwd_down", "bwd_down", "bwd_up"))
+    fb_flops = sum(l.flops()[0] + l.flops()[1] for l in layers)
+
+    extras = {}
+    if not args.no_extras:
+        log("[bench] quantize bandwidth")
+        extras["quantize"] = bench_quantize(hip, layers)
+        log("[bench] decode shapes")
+        extras["decode"] = bench_decode(hip)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(up)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "70B-class MLP slice: up W 28672x8192 and down W 8192x28672 "
+                               "(NF4, double quant), 4096 tokens, LoRA r=64 alpha=16",
+                   "M": cfg.M, "r": cfg.r, "alpha": cfg.alpha,
+                   "step": "2x nf4_quantize + 2x fwd + 2x bwd + 2x decode fwd (M=16)",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "fwd_bwd_tflops": round(fb_flops / (fb_ms * 1e-3) / 1e12, 2),
+        "breakdown_ms": breakdown,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

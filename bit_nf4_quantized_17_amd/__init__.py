@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_workspace_bytes.restype = SZ
     L.qlora_linear_bwd.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P, SZ, P]
     L.qlora_linear_bwd.restype = I
+    L.qlora_set_timing_events.argtypes = [P, P, P, P]
+    L.qlora_set_timing_events.restype = I
     _lib = L
     return L
 
@@ -91,6 +93,12 @@ def _need(t, dtype, shape, name):
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, "
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def qlora_set_timing_events(fwd_begin=None, fwd_end=None, dx_begin=None, dx_end=None) -> None:
+    """Raw hipEvent_t handles (ints) recorded around the main GEMM kernels of
+    later calls on this thread; all None clears the hook."""
+    _check(lib().qlora_set_timing_events(fwd_begin, fwd_end, dx_begin, dx_end))
 
 
 def qlora_abi_version() -> int:

@@ -22,6 +22,7 @@ LIB = os.path.join(HERE, "libqlora_nf4.so")
 SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "gemm.hip": [],
+    "gemm_big.hip": [],
     "capi.hip": [],
 }
 

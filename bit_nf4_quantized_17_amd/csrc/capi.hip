@@ -16,6 +16,15 @@ namespace {
 
 thread_local std::string g_err;
 
+struct TimingHook {
+  hipEvent_t fwd_begin = nullptr, fwd_end = nullptr, dx_begin = nullptr, dx_end = nullptr;
+};
+thread_local TimingHook g_hook;
+
+void record(hipEvent_t ev, hipStream_t st) {
+  if (ev) (void)hipEventRecord(ev, st);
+}
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -106,6 +115,14 @@ extern "C" {
 
 int qlora_abi_version(void) { return QLORA_ABI_VERSION; }
 
+int qlora_set_timing_events(void* fwd_begin, void* fwd_end, void* dx_begin, void* dx_end) {
+  g_hook.fwd_begin = (hipEvent_t)fwd_begin;
+  g_hook.fwd_end = (hipEvent_t)fwd_end;
+  g_hook.dx_begin = (hipEvent_t)dx_begin;
+  g_hook.dx_end = (hipEvent_t)dx_end;
+  return ok();
+}
+
 const char* qlora_last_error(void) { return g_err.c_str(); }
 
 void nf4_levels(float out[16]) {
@@ -173,7 +190,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   const float s = alpha / (float)r;
   hipError_t e = launch_lora_down(X, A, M, w->cols, r, (float*)workspace, T_save, st);
   if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd: lora_down launch");
+  record(g_hook.fwd_begin, st);
   e = launch_fwd_main(view(w), X, M, T_save, B, r, s, Y, st);
+  record(g_hook.fwd_end, st);
   return hip_status(e, "qlora_linear_fwd: main launch");
 }
 
@@ -216,7 +235,9 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
   e = launch_lora_db(dY, T, M, N, r, s, part, dB, st);
   if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dB launch");
   if (dX) {
+    record(g_hook.dx_begin, st);
     e = launch_dx_main(view(w), dY, M, U, A, r, s, dX, st);
+    record(g_hook.dx_end, st);
     if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dX launch");
   }
   e = launch_lora_da(U, X, M, K, r, s, part, dA, st);

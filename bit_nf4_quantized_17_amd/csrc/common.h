@@ -72,6 +72,12 @@ hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const floa
 hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const float* U,
                           const u16* A, int r, float s, u16* dX, hipStream_t st);
 
+// Tile-128 variants with guarded loads (any alignment / size).
+hipError_t launch_fwd_generic(const NF4View& w, const u16* X, int64_t M, const float* T,
+                              const u16* B, int r, float s, u16* Y, hipStream_t st);
+hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const float* U,
+                             const u16* A, int r, float s, u16* dX, hipStream_t st);
+
 // Workspace (fp32 elements) the skinny partial sums of one call need.
 int64_t skinny_partial_elems(int64_t I, int64_t C, int r);
 

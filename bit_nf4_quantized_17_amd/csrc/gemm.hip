@@ -547,7 +547,10 @@ hipError_t launch_lora_da(const float* U, const u16* X, int64_t M, int64_t K, in
   return launch_reduce(ws, skinny_plan(K, M).splits, K, r, s, dA, K, true, st);
 }
 
-hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const float* T,
+// Tile-128 fused GEMMs for the shapes the buffer-load kernels of gemm_big.hip
+// do not take (activation rows that are not 16-byte aligned, or operands of
+// 2 GiB and more): same math, guarded loads.
+hipError_t launch_fwd_generic(const NF4View& w, const u16* X, int64_t M, const float* T,
                            const u16* B, int r, float s, u16* Y, hipStream_t st) {
   GemmArgs p = zero_args();
   p.a = X; p.lda = w.K; p.a_vec = vec_ok(X, w.K);
@@ -561,7 +564,7 @@ hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const floa
   return hipGetLastError();
 }
 
-hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const float* U,
+hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const float* U,
                           const u16* A, int r, float s, u16* dX, hipStream_t st) {
   GemmArgs p = zero_args();
   p.a = dY; p.lda = w.N; p.a_vec = vec_ok(dY, w.N);
@@ -574,5 +577,6 @@ hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const floa
                      dim3(NTHREADS), 0, st, p);
   return hipGetLastError();
 }
+
 
 }  // namespace qln

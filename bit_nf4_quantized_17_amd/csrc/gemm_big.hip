@@ -1,0 +1,494 @@
+// gemm_big.hip -- the two large fused GEMMs of the QLoRA linear layer:
+//
+//   forward  Y  = X W'^T + s T B^T      (contraction over k, W' rows are output columns)
+//   backward dX = dY W' + s U A          (contraction over n, W' columns are output columns)
+//
+// W' is the bf16 dequantized NF4 weight, produced tile by tile inside the
+// kernel: a thread turns one 64-code block into bf16 exactly as
+// nf4_dequantize does (w' = bf16(fl32(L[code] * scale))), through a per-block
+// 16-entry bf16 table held in registers and looked up with byte permutes, and
+// writes it to LDS with 16-byte stores.  Ultralytics glossary "QLoRA", "How
+// QLoRA works": dequantize NF4 to bfloat16 right before the matrix product,
+// gradients flow through the dequantized weights.
+//
+// Tiling (gfx950): 256 threads = 4 waves, output tile 256 x 256, contraction
+// step 64.  Each wave owns a 128 x 128 quarter as 4 x 4 accumulators of
+// v_mfma_f32_32x32x16_bf16 (256 accumulator registers).  LDS holds two stages
+// of both operand tiles (about 144 KiB); global loads run two stages ahead in
+// registers, so one barrier per step separates writing stage k+1 from
+// reading stage k.  The forward's weight tile is [n][k] (contraction
+// contiguous: plain 16-byte fragment reads); the backward's is [n][k] with
+// n the contraction, read with ds_read_b64_tr_b16 (within each 16-lane group
+// lane i receives element i%4 of the rows addressed by lanes 4j + i/4, which
+// yields the column fragment the MFMA needs).
+//
+// The LoRA term is a prologue: the accumulators start as (s T) B^T or
+// (s U) A, with s T / s U rounded to bf16 on the way to LDS (rank r <= 128 in
+// steps of 64), then the base product accumulates on top.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "device.h"
+
+namespace qln {
+namespace big {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int APITCH = BK + 8;          // A tile [256][72] bf16 (144-byte rows)
+constexpr int FPITCH = BK + 8;          // forward W tile [256 n][72]
+constexpr int TPITCH = BN + 16;         // backward W tile [64 n][272] (544-byte rows)
+constexpr int A_ELEMS = BM * APITCH;    // 18432
+constexpr int BF_ELEMS = BN * FPITCH;   // 18432
+constexpr int BT_ELEMS = BK * TPITCH;   // 17408
+constexpr int NTHREADS = 256;
+
+enum { MODE_FWD = 0, MODE_DX = 1 };
+
+template <int MODE>
+constexpr int b_elems() { return MODE == MODE_FWD ? BF_ELEMS : BT_ELEMS; }
+template <int MODE>
+constexpr size_t lds_bytes() { return (size_t)2 * (A_ELEMS + b_elems<MODE>()) * 2; }
+
+struct BigArgs {
+  const u16* a; int64_t lda; bool a_vec;   // X [M][K] or dY [M][N]
+  NF4View w;
+  int64_t M, J, C;                         // output M x J, contraction C
+  const float* la;                         // T or U, fp32 [M][r]
+  const u16* lb;                           // B [N][r] (forward) or A [r][K] (backward)
+  int r; float s; bool la_vec; bool lb_vec;
+  u16* out; int64_t ldo;
+};
+
+typedef __attribute__((address_space(3))) short lds_short;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// ---------------------------------------------------------------------------
+// dequantization of one 64-code block (32 bytes) into 32 bf16 pairs
+// ---------------------------------------------------------------------------
+struct Table {
+  uint32_t lo[4], hi[4];   // low / high bytes of the 16 bf16 values, 4 per word
+};
+
+__device__ __forceinline__ Table make_table(float sc) {
+  uint32_t P[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    P[j] = pack_bf16x2(__uint_as_float(kNF4LevelBits[2 * j]) * sc,
+                       __uint_as_float(kNF4LevelBits[2 * j + 1]) * sc);
+  Table t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x06040200u);
+    t.hi[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x07050301u);
+  }
+  return t;
+}
+
+// four 4-bit indices (one per byte) -> their bf16 low bytes and high bytes
+__device__ __forceinline__ void lookup4(const Table& t, uint32_t idx, uint32_t& lo, uint32_t& hi) {
+  const uint32_t m8 = idx & 0x08080808u;
+  const uint32_t selA = idx + (m8 << 1);          // codes 0..7 -> 0..7, codes 8..15 -> 24..31 (0xFF)
+  const uint32_t selB = selA ^ 0x18181818u;       // codes 8..15 -> 0..7, codes 0..7 -> 24..31 (0xFF)
+  lo = __builtin_amdgcn_perm(t.lo[1], t.lo[0], selA) & __builtin_amdgcn_perm(t.lo[3], t.lo[2], selB);
+  hi = __builtin_amdgcn_perm(t.hi[1], t.hi[0], selA) & __builtin_amdgcn_perm(t.hi[3], t.hi[2], selB);
+}
+
+// 8 codes (one word, element e in bits 4e..4e+3) -> 4 words of bf16 pairs in element order
+__device__ __forceinline__ void dequant8(const Table& t, uint32_t c, uint32_t o[4]) {
+  uint32_t le, he, lo_, ho;
+  lookup4(t, c & 0x0F0F0F0Fu, le, he);            // elements 0, 2, 4, 6
+  lookup4(t, (c >> 4) & 0x0F0F0F0Fu, lo_, ho);    // elements 1, 3, 5, 7
+  const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);
+  const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);
+  const uint32_t o13 = __builtin_amdgcn_perm(ho, lo_, 0x05010400u);
+  const uint32_t o57 = __builtin_amdgcn_perm(ho, lo_, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(o13, e02, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(o13, e02, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);
+}
+
+__device__ __forceinline__ float block_scale(const NF4View& w, int64_t blk) {
+  return e4m3_decode(w.qscale[blk]) * w.dscale[blk >> 8];
+}
+
+// ---------------------------------------------------------------------------
+// Main-loop operand loads go through buffer resources: a load whose byte
+// offset is past the buffer's end returns zeros, so rows beyond M, rows of W
+// beyond N and the stages past the last one need no branches.  (A row read
+// past the contraction length C of the backward's dY runs into the next row;
+// those values meet W rows beyond N, which read as zero codes with a zero
+// scale, so they add nothing.)
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+struct Bufs {
+  __amdgpu_buffer_rsrc_t a, codes, qscale, dscale;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+struct StageA { uint4 v[8]; };           // A tile: 8 x 16 bytes per thread
+struct StageW { uint4 c[2]; float sc; };  // one block of 64 codes and its scale
+
+// A tile rows m0 + tid/8 + 32q, contraction c0 + 8*(tid%8) .. +8
+__device__ __forceinline__ void load_a(StageA& st, const Bufs& b, uint32_t row_off0,
+                                       uint32_t row_step, uint32_t c0) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) st.v[q] = bload16(b.a, row_off0 + q * row_step + 2 * c0);
+}
+
+__device__ __forceinline__ float scale_at(const Bufs& b, uint32_t blk) {
+  const uint32_t q = __builtin_amdgcn_raw_buffer_load_b8(b.qscale, blk, 0, 0);
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.dscale, 4 * (blk >> 8), 0, 0));
+  return e4m3_decode(q) * d;
+}
+
+// the thread's weight block: row n, columns k .. k+63; a stage past the last
+// one (live == false) gets scale 0, so it multiplies as a zero tile
+__device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, uint32_t k,
+                                       uint32_t K, bool live) {
+  const uint32_t off = n * (K / 2) + k / 2;
+  st.c[0] = bload16(b.codes, off);
+  st.c[1] = bload16(b.codes, off + 16);
+  const float sc = scale_at(b, n * (K / 64) + k / 64);
+  st.sc = live ? sc : 0.0f;
+}
+
+__device__ __forceinline__ void store_a(const StageA& st, u16* sA, int tid) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    *reinterpret_cast<uint4*>(sA + (tid / 8 + 32 * q) * APITCH + (tid % 8) * 8) = st.v[q];
+}
+
+// LoRA prologue A-side tile: s times fp32 T or U, rounded to bf16 (guarded loads)
+__device__ __forceinline__ void lora_a_tile(const float* src, int64_t ld, int64_t rows,
+                                            int64_t C, int64_t m0, int64_t c0, bool vec,
+                                            float s, u16* sA, int tid) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t row = m0 + tid / 8 + 32 * q;
+    const int64_t c = c0 + (tid % 8) * 8;
+    float x[8];
+    if (row < rows && c + 8 <= C && vec) {
+      const float4 u = *reinterpret_cast<const float4*>(src + row * ld + c);
+      const float4 v = *reinterpret_cast<const float4*>(src + row * ld + c + 4);
+      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (row < rows && c + e < C) ? src[row * ld + c + e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= s;
+    *reinterpret_cast<uint4*>(sA + (tid / 8 + 32 * q) * APITCH + (tid % 8) * 8) =
+        make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7]));
+  }
+}
+
+// dequantize the thread's block and store its 64 bf16 values contiguously at dst
+__device__ __forceinline__ void store_w(const StageW& st, u16* dst) {
+  const Table t = make_table(st.sc);
+  const uint32_t c[8] = {st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w,
+                         st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t o[4];
+    dequant8(t, c[i], o);
+    *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ u16* w_dst(u16* sB, int tid) {
+  if constexpr (MODE == MODE_FWD) return sB + tid * FPITCH;
+  else return sB + (tid / 4) * TPITCH + 64 * (tid % 4);
+}
+
+// LoRA prologue operand of the B side, bf16: forward B [J][r] rows n0 + tid
+// (one 64-wide chunk of r); backward A [r][J] rows c0 + tid/4, columns
+// j0 + 64*(tid%4) .. +64.  Written in the same LDS layout as the weight tile.
+template <int MODE>
+__device__ __forceinline__ void lora_b_tile(const BigArgs& p, u16* sB, int64_t j0, int64_t c0,
+                                            int tid) {
+  u16* dst = w_dst<MODE>(sB, tid);
+  int64_t row, col0, rows, cols, ld;
+  if constexpr (MODE == MODE_FWD) {
+    row = j0 + tid; col0 = c0; rows = p.J; cols = p.r; ld = p.r;
+  } else {
+    row = c0 + tid / 4; col0 = j0 + 64 * (tid % 4); rows = p.r; cols = p.J; ld = p.J;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t c = col0 + 8 * q;
+    uint32_t v[4] = {0, 0, 0, 0};
+    if (row < rows && c + 8 <= cols && p.lb_vec) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p.lb + row * ld + c);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    } else if (row < rows) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < cols) v[e >> 1] |= (uint32_t)p.lb[row * ld + c + e] << (16 * (e & 1));
+    }
+    *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA on one LDS stage
+// ---------------------------------------------------------------------------
+template <int MODE>
+__device__ __forceinline__ bf16x8_t read_b(const u16* sB, int wn, int b, int ks, int lane) {
+  if constexpr (MODE == MODE_FWD) {
+    return *reinterpret_cast<const bf16x8_t*>(
+        sB + (wn * 128 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + (lane >> 5) * 8);
+  } else {
+    const int L = lane & 15;
+    const int col = wn * 128 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+    const int row = ks * 16 + 8 * (lane >> 5) + (L >> 2);
+    const lds_short* base = (const lds_short*)(sB);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + row * TPITCH + col));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + (row + 4) * TPITCH + col));
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void mma_stage(f32x16_t (&acc)[4][4], const u16* sA, const u16* sB,
+                                          int wm, int wn, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    bf16x8_t fa[4], fb[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      fa[a] = *reinterpret_cast<const bf16x8_t*>(
+          sA + (wm * 128 + a * 32 + (lane & 31)) * APITCH + ks * 16 + (lane >> 5) * 8);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[b] = read_b<MODE>(sB, wn, b, ks, lane);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+  }
+}
+
+// One contraction step with the producer work for the next stage woven in:
+// for each 16-wide substep ks, the fragments of ks+1 are read while the 16
+// MFMAs of ks issue, then a quarter of the next stage is written to the other
+// LDS buffer (two 16-byte A rows and 16 dequantized weights).  Scheduling
+// barriers keep the compiler from hoisting all fragment reads of the stage
+// (128 registers) ahead of the MFMAs.
+template <int MODE>
+__device__ __forceinline__ void frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], const u16* sA,
+                                      const u16* sB, int wm, int wn, int ks, int lane) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    fa[a] = *reinterpret_cast<const bf16x8_t*>(
+        sA + (wm * 128 + a * 32 + (lane & 31)) * APITCH + ks * 16 + (lane >> 5) * 8);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) fb[b] = read_b<MODE>(sB, wn, b, ks, lane);
+}
+
+template <int MODE>
+__device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][4], const u16* sA,
+                                               const u16* sB, int wm, int wn, int lane,
+                                               const StageA& ra, const StageW& w,
+                                               u16* sA_next, u16* wdst_next, int tid) {
+  bf16x8_t fa[2][4], fb[2][4];
+  frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
+  const Table t = make_table(w.sc);
+  const uint32_t c[8] = {w.c[0].x, w.c[0].y, w.c[0].z, w.c[0].w,
+                         w.c[1].x, w.c[1].y, w.c[1].z, w.c[1].w};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int cur = ks & 1;
+    if (ks < 3) frags<MODE>(fa[cur ^ 1], fb[cur ^ 1], sA, sB, wm, wn, ks + 1, lane);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b],
+                                                            0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * ks + h;
+      uint32_t o[4];
+      dequant8(t, c[i], o);
+      *reinterpret_cast<uint4*>(wdst_next + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(sA_next + (tid / 8 + 32 * i) * APITCH + (tid % 8) * 8) = ra.v[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
+  extern __shared__ __attribute__((aligned(16))) u16 smem[];
+  u16* sA[2] = {smem, smem + A_ELEMS};
+  u16* sB[2] = {smem + 2 * A_ELEMS, smem + 2 * A_ELEMS + b_elems<MODE>()};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int64_t j0 = (int64_t)blockIdx.y * BN;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  // ---- LoRA prologue: acc = sum_{c < r} bf16(s la(m, c)) lb(j, c) ----
+  for (int64_t c0 = 0; c0 < p.r; c0 += BK) {
+    __syncthreads();
+    lora_a_tile(p.la, p.r, p.M, p.r, m0, c0, p.la_vec, p.s, sA[0], tid);
+    lora_b_tile<MODE>(p, sB[0], j0, c0, tid);
+    __syncthreads();
+    mma_stage<MODE>(acc, sA[0], sB[0], wm, wn, lane);
+  }
+  __syncthreads();
+
+  // ---- main contraction ----
+  // While stage kt is multiplied out of LDS buffer kt&1, the other buffer
+  // receives stage kt+1 (A tile from registers loaded one step earlier, the
+  // weight block dequantized from registers loaded two steps earlier).  Loads
+  // of stages past the end read zeros or unused data and are never consumed.
+  Bufs bf;
+  bf.a = rsrc(p.a, (uint32_t)(p.M * p.lda * 2));
+  bf.codes = rsrc(p.w.codes, (uint32_t)(p.w.N * p.w.K / 2));
+  bf.qscale = rsrc(p.w.qscale, (uint32_t)(p.w.N * p.w.K / 64));
+  bf.dscale = rsrc(p.w.dscale, (uint32_t)(4 * ((p.w.N * p.w.K / 64 + 255) / 256)));
+  const uint32_t K = (uint32_t)p.w.K;
+  const uint32_t a_row0 = (uint32_t)((m0 + tid / 8) * p.lda * 2) + 2 * 8 * (tid % 8);
+  const uint32_t a_step = (uint32_t)(32 * p.lda * 2);
+  const uint32_t a_base = a_row0;   // rows past M give offsets past the end (host checks 32-bit room)
+  // weight block coordinates of this thread for contraction step kt
+  auto w_n = [&](int64_t kt) -> uint32_t {
+    if constexpr (MODE == MODE_FWD) return (uint32_t)(j0 + tid);
+    else return (uint32_t)(kt * BK + tid / 4);
+  };
+  auto w_k = [&](int64_t kt) -> uint32_t {
+    if constexpr (MODE == MODE_FWD) return (uint32_t)(kt * BK);
+    else return (uint32_t)(j0 + 64 * (tid % 4));
+  };
+  u16* wdst0 = w_dst<MODE>(sB[0], tid);
+  u16* wdst1 = w_dst<MODE>(sB[1], tid);
+
+  const int64_t nk = (p.C + BK - 1) / BK;
+  StageA ra;
+  StageW w0, w1;
+  load_a(ra, bf, a_base, a_step, 0);
+  load_w(w0, bf, w_n(0), w_k(0), K, true);
+  store_a(ra, sA[0], tid);
+  store_w(w0, wdst0);
+  load_a(ra, bf, a_base, a_step, BK);
+  load_w(w1, bf, w_n(1), w_k(1), K, 1 < nk);
+  load_w(w0, bf, w_n(2), w_k(2), K, 2 < nk);
+  __syncthreads();
+  // steps are taken in pairs; with an odd count the last pair's second step
+  // multiplies a zero weight tile (no early exit: that would make the
+  // compiler keep two copies of the accumulators)
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    // buffer 0 holds stage kt; ra = A(kt+1), w1 = W(kt+1), w0 = W(kt+2)
+    step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid);
+    load_a(ra, bf, a_base, a_step, (uint32_t)((kt + 2) * BK));
+    load_w(w1, bf, w_n(kt + 3), w_k(kt + 3), K, kt + 3 < nk);
+    __syncthreads();
+    // buffer 1 holds stage kt+1; ra = A(kt+2), w0 = W(kt+2), w1 = W(kt+3)
+    step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid);
+    load_a(ra, bf, a_base, a_step, (uint32_t)((kt + 3) * BK));
+    load_w(w0, bf, w_n(kt + 4), w_k(kt + 4), K, kt + 4 < nk);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t j = j0 + wn * 128 + b * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = m0 + wm * 128 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (i < p.M && j < p.J) p.out[i * p.ldo + j] = f32_to_bf16(acc[a][b][v]);
+      }
+    }
+}
+
+static bool vec_ok(const void* ptr, int64_t ld) {
+  return ((uintptr_t)ptr % 16 == 0) && (ld % 8 == 0);
+}
+
+template <int MODE>
+static hipError_t launch(const BigArgs& p, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<MODE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds_bytes<MODE>());
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  dim3 grid((unsigned)((p.M + BM - 1) / BM), (unsigned)((p.J + BN - 1) / BN), 1);
+  hipLaunchKernelGGL(k_gemm_big<MODE>, grid, dim3(NTHREADS), lds_bytes<MODE>(), st, p);
+  return hipGetLastError();
+}
+
+}  // namespace big
+
+// The buffer-load kernels need 16-byte aligned activation rows and 32-bit
+// byte offsets (with room for the tile overrun); other shapes take the
+// tile-128 kernels of gemm.hip.
+static bool fits_32bit(int64_t M, int64_t lda, const NF4View& w) {
+  const int64_t lim = (int64_t)1 << 31;
+  return (M + big::BM) * lda * 2 + 8 * big::BK * 2 < lim && (w.N + big::BN) * w.K / 2 < lim &&
+         w.N * w.K / 64 < lim;
+}
+
+hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const float* T,
+                           const u16* B, int r, float s, u16* Y, hipStream_t st) {
+  if (!big::vec_ok(X, w.K) || !fits_32bit(M, w.K, w))
+    return launch_fwd_generic(w, X, M, T, B, r, s, Y, st);
+  big::BigArgs p;
+  p.a = X; p.lda = w.K; p.a_vec = big::vec_ok(X, w.K);
+  p.w = w;
+  p.M = M; p.J = w.N; p.C = w.K;
+  p.la = T; p.lb = B; p.r = r; p.s = s;
+  p.la_vec = big::vec_ok(T, r * 2); p.lb_vec = big::vec_ok(B, r);
+  p.out = Y; p.ldo = w.N;
+  return big::launch<big::MODE_FWD>(p, st);
+}
+
+hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const float* U,
+                          const u16* A, int r, float s, u16* dX, hipStream_t st) {
+  if (!big::vec_ok(dY, w.N) || !fits_32bit(M, w.N, w) || (w.N + big::BK) * w.K / 2 >= ((int64_t)1 << 31))
+    return launch_dx_generic(w, dY, M, U, A, r, s, dX, st);
+  big::BigArgs p;
+  p.a = dY; p.lda = w.N; p.a_vec = big::vec_ok(dY, w.N);
+  p.w = w;
+  p.M = M; p.J = w.K; p.C = w.N;
+  p.la = U; p.lb = A; p.r = r; p.s = s;
+  p.la_vec = big::vec_ok(U, r * 2); p.lb_vec = big::vec_ok(A, w.K);
+  p.out = dX; p.ldo = w.K;
+  return big::launch<big::MODE_DX>(p, st);
+}
+
+}  // namespace qln

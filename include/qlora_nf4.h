@@ -172,6 +172,15 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
                      uint16_t* dX, uint16_t* dA, uint16_t* dB,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Benchmark timing hook.  When set, later calls ON THIS THREAD record
+ * fwd_begin / fwd_end (hipEvent_t handles the caller created) on the call's
+ * stream immediately before and after the launch of the forward's main GEMM
+ * kernel, and dx_begin / dx_end around the backward's dX GEMM kernel, so the
+ * caller can read those kernels' durations with hipEventElapsedTime.  NULL
+ * entries record nothing; qlora_set_timing_events(NULL, NULL, NULL, NULL)
+ * clears the hook.  Returns QL_OK. */
+int qlora_set_timing_events(void* fwd_begin, void* fwd_end, void* dx_begin, void* dx_end);
+
 #ifdef __cplusplus
 }
 #endif
