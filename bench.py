@@ -202,16 +202,22 @@ def bench_decode(hip, reps=60):
                              dtype=torch.uint8, device="cuda")
             for i in range(5):
                 q.qlora_linear_fwd(copies[i % ncopy], X, A, B, cfg.alpha, Y=Y, T=T, workspace=ws)
+            kev = [(hip.event(), hip.event()) for _ in range(reps)]
             e0, e1 = hip.event(), hip.event()
             torch.cuda.synchronize()
             hip.record(e0, st)
             for i in range(reps):
+                q.qlora_set_timing_events(kev[i][0], kev[i][1])
                 q.qlora_linear_fwd(copies[i % ncopy], X, A, B, cfg.alpha, Y=Y, T=T, workspace=ws)
+            q.qlora_set_timing_events()
             hip.record(e1, st)
             ms = hip.elapsed_ms(e0, e1) / reps
-            gbs = decode_bytes(M, L.N, L.K, cfg.r) / (ms * 1e-3) / 1e9
-            out.append({"W": f"{L.N}x{L.K}", "M": M, "us_per_call": round(ms * 1e3, 2),
-                        "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+            kms = sum(hip.elapsed_ms(a, b) for a, b in kev) / reps
+            nbytes = decode_bytes(M, L.N, L.K, cfg.r)
+            gbs = nbytes / (kms * 1e-3) / 1e9
+            out.append({"W": f"{L.N}x{L.K}", "M": M, "kernel_us": round(kms * 1e3, 2),
+                        "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                        "call_us": round(ms * 1e3, 2)})
         del copies, w0
         torch.cuda.empty_cache()
     return out

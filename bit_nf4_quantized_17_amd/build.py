@@ -23,6 +23,7 @@ SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "gemm.hip": [],
     "gemm_big.hip": [],
+    "decode.hip": [],
     "capi.hip": [],
 }
 

@@ -188,6 +188,12 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   if (workspace && !aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
+  if (decode_fits(M, view(w), r)) {   // decode sizes: one kernel, T computed inside
+    record(g_hook.fwd_begin, st);
+    hipError_t e = launch_decode(view(w), X, M, A, B, r, s, Y, T_save, (float*)workspace, st);
+    record(g_hook.fwd_end, st);
+    return hip_status(e, "qlora_linear_fwd: decode launch");
+  }
   hipError_t e = launch_lora_down(X, A, M, w->cols, r, (float*)workspace, T_save, st);
   if (e != hipSuccess) return hip_status(e, "qlora_linear_fwd: lora_down launch");
   record(g_hook.fwd_begin, st);

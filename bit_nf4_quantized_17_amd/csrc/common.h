@@ -12,6 +12,8 @@ namespace qln {
 
 typedef uint16_t u16;
 
+constexpr int QLN_MAX_RANK = 128;   // largest LoRA rank the kernels take
+
 // The 16 NF4 levels as fp32 bit patterns, code order.  Ultralytics glossary
 // "QLoRA", "How QLoRA works" (the level-building snippet): normal quantiles at
 // probabilities evenly spaced from 0.9677083 towards 0.5 (8 positive, 7
@@ -77,6 +79,13 @@ hipError_t launch_fwd_generic(const NF4View& w, const u16* X, int64_t M, const f
                               const u16* B, int r, float s, u16* Y, hipStream_t st);
 hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const float* U,
                              const u16* A, int r, float s, u16* dX, hipStream_t st);
+
+// Forward at M <= 16 (writes Y and T_save): one kernel for r <= 32, else the
+// split T kernels first (ws: their fp32 partials); decode_fits says whether a
+// shape can take it.
+bool decode_fits(int64_t M, const NF4View& w, int r);
+hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
+                         int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st);
 
 // Workspace (fp32 elements) the skinny partial sums of one call need.
 int64_t skinny_partial_elems(int64_t I, int64_t C, int r);

@@ -137,7 +137,7 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 struct StageA { uint4 v[8]; };           // A tile: 8 x 16 bytes per thread
-struct StageW { uint4 c[2]; float sc; };  // one block of 64 codes and its scale
+struct StageW { uint4 c[2]; uint32_t q; float d; };  // codes, raw scale byte, group constant
 
 // A tile rows m0 + tid/8 + 32q, contraction c0 + 8*(tid%8) .. +8
 __device__ __forceinline__ void load_a(StageA& st, const Bufs& b, uint32_t row_off0,
@@ -146,22 +146,23 @@ __device__ __forceinline__ void load_a(StageA& st, const Bufs& b, uint32_t row_o
   for (int q = 0; q < 8; ++q) st.v[q] = bload16(b.a, row_off0 + q * row_step + 2 * c0);
 }
 
-__device__ __forceinline__ float scale_at(const Bufs& b, uint32_t blk) {
-  const uint32_t q = __builtin_amdgcn_raw_buffer_load_b8(b.qscale, blk, 0, 0);
-  const float d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.dscale, 4 * (blk >> 8), 0, 0));
-  return e4m3_decode(q) * d;
-}
-
-// the thread's weight block: row n, columns k .. k+63; a stage past the last
-// one (live == false) gets scale 0, so it multiplies as a zero tile
+// the thread's weight block: row n, columns k .. k+63.  The scale is decoded
+// only when the block is dequantized (one step later), so nothing waits for
+// these loads now; a stage past the last one (live == false) gets group
+// constant 0, so it multiplies as a zero tile.
 __device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, uint32_t k,
                                        uint32_t K, bool live) {
   const uint32_t off = n * (K / 2) + k / 2;
   st.c[0] = bload16(b.codes, off);
   st.c[1] = bload16(b.codes, off + 16);
-  const float sc = scale_at(b, n * (K / 64) + k / 64);
-  st.sc = live ? sc : 0.0f;
+  const uint32_t blk = n * (K / 64) + k / 64;
+  st.q = __builtin_amdgcn_raw_buffer_load_b8(b.qscale, blk, 0, 0);
+  // a dead stage reads past the end of the group constants, which returns 0
+  st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                       b.dscale, live ? 4 * (blk >> 8) : 0xFFFFFFF0u, 0, 0));
 }
+
+__device__ __forceinline__ float stage_scale(const StageW& st) { return e4m3_decode(st.q) * st.d; }
 
 __device__ __forceinline__ void store_a(const StageA& st, u16* sA, int tid) {
 #pragma unroll
@@ -196,7 +197,7 @@ __device__ __forceinline__ void lora_a_tile(const float* src, int64_t ld, int64_
 
 // dequantize the thread's block and store its 64 bf16 values contiguously at dst
 __device__ __forceinline__ void store_w(const StageW& st, u16* dst) {
-  const Table t = make_table(st.sc);
+  const Table t = make_table(stage_scale(st));
   const uint32_t c[8] = {st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w,
                          st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w};
 #pragma unroll
@@ -309,7 +310,7 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][4], const u16*
                                                u16* sA_next, u16* wdst_next, int tid) {
   bf16x8_t fa[2][4], fb[2][4];
   frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
-  const Table t = make_table(w.sc);
+  const Table t = make_table(stage_scale(w));
   const uint32_t c[8] = {w.c[0].x, w.c[0].y, w.c[0].z, w.c[0].w,
                          w.c[1].x, w.c[1].y, w.c[1].z, w.c[1].w};
 #pragma unroll

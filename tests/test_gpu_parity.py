@@ -115,6 +115,9 @@ SMALL = [
     (64, 64, 1, 1, 2.0),
     (200, 128, 300, 128, 16.0),   # maximum rank
     (384, 512, 257, 64, 16.0),
+    (320, 256, 9, 48, 16.0),      # decode size, rank above the in-kernel T limit
+    (8200, 128, 16, 128, 8.0),    # decode size, maximum rank, two column tiles per group
+    (16400, 64, 3, 16, 32.0),     # decode size, four column tiles per group, ragged N
 ]
 
 
