@@ -284,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip decode/quantize bandwidth runs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device-to-device 3 times (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -295,6 +297,14 @@ def main():
     import synthetic_inputs as si
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        a = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": a.numel() * 4, "copies": 3}))
+        return
     hip = Hip()
     cfg = si.CONFIGS["c4"]
     log("[bench] generating the 70B-class MLP slice inputs")
@@ -351,13 +361,13 @@ def main():
     dx_ms = (kern["dx_up"] + kern["dx_down"]) / 2
     main_flops = 2 * cfg.M * up.N * up.K + 2 * cfg.M * up.N * cfg.r   # base + LoRA prologue
     if dx_ms >= fwd_ms:
-        dom, dom_ms = "k_gemm dX (NF4 transposed producer, U A prologue)", dx_ms
+        dom, dom_ms = "k_gemm_big<1> dX (NF4 transposed producer, U A prologue)", dx_ms
         dom_key = "gemm_dx"
     else:
-        dom, dom_ms = "k_gemm fwd (NF4 producer, T B^T prologue)", fwd_ms
+        dom, dom_ms = "k_gemm_big<0> fwd (NF4 producer, T B^T prologue)", fwd_ms
         dom_key = "gemm_fwd"
     achieved = main_flops / (dom_ms * 1e-3) / 1e12
-    src = source_hash("gemm.hip")
+    src = source_hash("gemm_big.hip")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic(dom_key, src), "kernel": dom,
