@@ -89,7 +89,9 @@ int check_layer(const qlora_nf4_weight* w, int64_t M, int r, int compute_dtype) 
 
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   (void)N;
-  return align256((size_t)skinny_partial_elems(M, K, r) * sizeof(float));
+  int64_t elems = skinny_partial_elems(M, K, r);
+  if (M <= 16) elems = std::max(elems, decode_workspace_elems(K, r));
+  return align256((size_t)elems * sizeof(float));
 }
 
 // backward workspace: U fp32 [M][r] | T fp32 [M][r] (when recomputed) | fp32 split partials
@@ -188,7 +190,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   if (workspace && !aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
-  if (decode_fits(M, view(w), r)) {   // decode sizes: one kernel, T computed inside
+  if (decode_fits(M, view(w), r)) {   // decode sizes: T partials, then the weight stream
     record(g_hook.fwd_begin, st);
     hipError_t e = launch_decode(view(w), X, M, A, B, r, s, Y, T_save, (float*)workspace, st);
     record(g_hook.fwd_end, st);

@@ -80,10 +80,11 @@ hipError_t launch_fwd_generic(const NF4View& w, const u16* X, int64_t M, const f
 hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const float* U,
                              const u16* A, int r, float s, u16* dX, hipStream_t st);
 
-// Forward at M <= 16 (writes Y and T_save): one kernel for r <= 32, else the
-// split T kernels first (ws: their fp32 partials); decode_fits says whether a
-// shape can take it.
+// Forward at M <= 16 (writes Y and T_save): the split-K T partials (into ws)
+// then the weight-streaming kernel; decode_fits says whether a shape can take
+// it and decode_workspace_elems how many fp32 elements of ws it needs.
 bool decode_fits(int64_t M, const NF4View& w, int r);
+int64_t decode_workspace_elems(int64_t K, int r);
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st);
 

@@ -1,29 +1,48 @@
-// decode.hip -- the forward at decode sizes (M <= 16 tokens), one kernel per
-// call.  Ultralytics glossary "QLoRA", "How QLoRA works": the frozen layer
-// dequantizes NF4 to bfloat16 for the matrix product and adds the LoRA path.
+// decode.hip -- the forward at decode sizes (M <= 16 tokens).  Ultralytics
+// glossary "QLoRA", "How QLoRA works": the frozen layer dequantizes NF4 to
+// bfloat16 for the matrix product and adds the LoRA path.
 //
-// At M <= 16 the layer is bound by streaming the packed weight (0.52 bytes
+// At M <= 16 the layer is bound by streaming the packed weight (0.516 bytes
 // per weight) from HBM, which leaves about three vector-ALU operations per
 // weight at full bandwidth -- less than an exact per-element dequantization
 // costs.  So this path factors the block scale out of the product:
 //   Y[m][n] = sum_blocks s_b * ( sum_{k in block} X[m][k] * bf16(L[code]) )
 //           + s_lora * sum_j T[m][j] B[n][j]
 // bf16(L[code]) comes from an LDS table indexed by one code byte (two codes
-// -> one bf16 pair), replicated 32 times so that a wave's lookups never share
-// a bank; each 64-code block is one pair of v_mfma_f32_16x16x32_bf16 into a
-// fresh accumulator, which is then scaled by the block's restored scale and
-// added in fp32.  (The prefill and training kernels multiply the exactly
-// dequantized bf16 weight instead; both round the weight's relative value
-// once to bf16 precision.)
+// -> one bf16 pair), with one copy per lane so that lookups never share a
+// bank; each 64-code block is one pair of v_mfma_f32_16x16x32_bf16 into a
+// fresh accumulator, which is then scaled by the block's restored scale
+// s_b = fl32(E4M3(q) * d) and added in fp32.  (The prefill and training
+// kernels multiply the exactly dequantized bf16 weight instead; both round
+// the weight's relative value once to bf16 precision.)
 //
-// Work split: a workgroup of 8 waves owns 64 output columns n (four 16-wide
-// MFMA tiles; 16 for narrow weights) over the full contraction K; wave w
-// takes an eighth of the 64-blocks for all tiles, so each X / A fragment it
-// loads from L2 serves four weight tiles, keeps the code loads of 4 blocks x
-// 4 tiles in flight, and the eight partial results are summed in LDS in wave
-// order.  For ranks above 32, T comes from the split-contraction kernel first.  T = X A^T (needed by every workgroup for its LoRA term) is computed
-// alongside from the same X fragments; workgroup 0 also writes it to T_save.
+// Two kernels per call.  k_tpart computes T = X A^T as fixed split-K partial
+// sums (a few dozen workgroups; A is read once).  k_decode streams the
+// weight: one workgroup of 8 waves per 16*TILES output columns (W rows),
+// sized so that the grid is about one workgroup per compute unit; each wave
+// takes an eighth of the contraction (rotated by the workgroup index, so that
+// the workgroups do not all stream the same column range of the weight at
+// once) for all its tiles, so each X fragment it loads serves TILES weight
+// tiles.  Codes are read straight from HBM into registers, 16 bytes a lane:
+// lane (i, g) of a 16-row tile loads bytes 16g..16g+15 of a pair of blocks of
+// row i, so the lower half-wave holds the first block and the upper half the
+// second; two v_permlane32_swap exchanges then leave every lane with 16 codes
+// of each block, at contraction offset 32(g&1) + 16(g>>1) inside the block,
+// and X is loaded with the same permutation, which leaves each block's sum
+// unchanged.  Each wave issues the next batch's loads one tile at a time
+// between the tiles of the current batch, so that the per-CU address unit
+// (about 16 bytes a clock, shared by the code and X loads) works through them
+// while the wave computes instead of stalling its issue.
+//
+// The restored scales of all the workgroup's blocks, the LoRA factor B of its
+// columns and T (summed from the partials in a fixed order; workgroup 0 also
+// writes it to T_save) are put in LDS at the start, behind the first batch's
+// loads.  The eight partial results are summed in LDS in wave order, so
+// results do not depend on timing.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "device.h"
@@ -33,16 +52,21 @@ namespace dec {
 
 constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
-constexpr int LUT_COPIES = 32;
-constexpr int MAX_RQ = 2;       // rank tiles of 16 computed here (r <= 32)
+constexpr int LUT_WORDS = 256 * 64;                   // one copy per lane, 64 KB (static LDS)
+constexpr uint32_t MAX_DYN_LDS = 96u * 1024u;         // what is left of the 160 KB
+constexpr int MAX_TILES = 8;
+constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every range this path uses
+constexpr int TP_WAVES = 4;             // waves of a k_tpart workgroup
+constexpr int MAX_SPLIT = 16;           // T partials a decode workgroup sums
 
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 struct DecArgs {
   const u16* X; int64_t M;          // X [M][K], M <= 16
   NF4View w;                        // W [N][K]
-  const u16* A; const u16* B; int r; float s;
+  const u16* B; int r; float s;
+  const float* tpart; int nsplit;   // T partial sums [nsplit][16][r]
   u16* Y; float* T_save;
 };
 
@@ -54,207 +78,422 @@ __device__ __forceinline__ bf16x8_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// One workgroup = 8 waves on TILES 16-column tiles of Y; wave w takes blocks
-// [w*nbk/8, (w+1)*nbk/8) of the contraction for all TILES tiles, four blocks
-// at a time.  The weight stream is read coalesced -- lane l loads the 32 code
-// bytes of block l%4 of row l/4 (each row's 4 blocks are 128 contiguous
-// bytes) and that block's two scale bytes -- then passes through a
-// wave-private LDS staging area to reach the MFMA layout.  The next batch's
-// loads are issued before the current batch is multiplied.
-constexpr int STG_PITCH = 144;                 // bytes per staged row (128 + 16)
-constexpr int STG_BYTES = 16 * STG_PITCH;      // codes of one tile x 4 blocks
-constexpr int STG_SC = 16 * 4 * 4;             // scales of one tile x 4 blocks
+// ---------------------------------------------------------------------------
+// T partials: workgroup (q, s) sums X[m][k] A[16q + j][k] over k in split s
+// (kchunk elements, a multiple of 64) into part[s][m][16q + j]; rows m >= M
+// are zero and columns 16q + j >= r are skipped.  Four waves take 32-wide
+// contraction steps in turn and are summed in LDS in wave order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * TP_WAVES) void k_tpart(const u16* X, int M, uint32_t K, const u16* A, int r,
+                                                         uint32_t kchunk, float* part) {
+  __shared__ float red[TP_WAVES][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, i16 = lane & 15, g = lane >> 4;
+  const int q = blockIdx.x;
+  const uint32_t k0 = blockIdx.y * kchunk, k1 = min(K, k0 + kchunk);
+  const auto rX = rsrc(X, (uint32_t)M * K * 2u);
+  const auto rA = rsrc(A, (uint32_t)r * K * 2u);
+  const uint32_t xrow = (uint32_t)i16 * K * 2u + 16u * (uint32_t)g;
+  const uint32_t arow = (uint32_t)(16 * q + i16) * K * 2u + 16u * (uint32_t)g;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;   // steps in flight per wave
+  for (uint32_t kk = k0 + 32u * wave; kk < k1; kk += 32u * TP_WAVES * U) {
+    bf16x8_t xv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = kk + 32u * TP_WAVES * u;
+      xv[u] = ld16(rX, k < k1 ? xrow + 2u * k : OOB);
+      av[u] = ld16(rA, k < k1 ? arow + 2u * k : OOB);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av[u], acc, 0, 0, 0);
+  }
+  // D layout: lane (col j = i16, rows 4g..4g+3)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[wave][(4 * g + e) * 16 + i16] = acc[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 256; e += 64 * TP_WAVES) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < TP_WAVES; ++w) v += red[w][e];
+    const int m = e >> 4, j = 16 * q + (e & 15);
+    if (j < r) part[((size_t)blockIdx.y * 16 + m) * r + j] = v;
+  }
+}
 
-// TIN: T was computed beforehand (ranks above 32) and is read from T_save.
-template <int TILES, bool TIN>
+// ---------------------------------------------------------------------------
+// the weight stream
+// ---------------------------------------------------------------------------
+// Byte offsets of the dynamic LDS regions.  The same function runs on the
+// host (to size the launch) and on the device.
+struct Lds {
+  uint32_t btab, ttab, stab, red, total;
+  uint32_t spitch;                  // floats per row of the scale table
+};
+__host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
+__host__ __device__ inline Lds lds_layout(int tiles, int nbk, int r) {
+  Lds L;
+  const uint32_t rows = 16u * (uint32_t)tiles;
+  // an even pitch of nbk + 2 or more keeps 8-byte reads aligned and puts the
+  // 16 rows a wave reads at once in different banks
+  L.spitch = ((uint32_t)nbk + 3u) & ~1u;
+  L.btab = 0;                                               // B rows of this workgroup, bf16 [rows][r]
+  L.ttab = align16(L.btab + rows * (uint32_t)r * 2u);       // T fp32 [16][r]
+  L.stab = align16(L.ttab + 16u * (uint32_t)r * 4u);        // restored block scales fp32 [rows][spitch]
+  L.red = L.stab;                                           // after the loop: per-wave partial sums
+  const uint32_t end_s = L.stab + rows * L.spitch * 4u;
+  const uint32_t end_r = L.red + (uint32_t)(WAVES * tiles) * 256u * 4u;
+  L.total = end_s > end_r ? end_s : end_r;
+  return L;
+}
+
+// Copy `len` bytes from buffer offset `goff` (16-byte aligned) to LDS `dst`
+// (16-byte aligned): 16-byte loads, up to four per thread in flight before
+// the stores, then single bytes for a tail under 16.
+__device__ __forceinline__ void stage_bytes(uint8_t* dst, __amdgpu_buffer_rsrc_t src, uint32_t goff,
+                                            uint32_t len, int tid) {
+  const uint32_t nchunk = len >> 4;
+  for (uint32_t base = (uint32_t)tid; base < nchunk; base += 4 * NTHREADS) {
+    u32x4v v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = base + (uint32_t)(u * NTHREADS);
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, i < nchunk ? goff + 16u * i : OOB, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = base + (uint32_t)(u * NTHREADS);
+      if (i < nchunk) *reinterpret_cast<u32x4v*>(dst + 16u * i) = v[u];
+    }
+  }
+  const uint32_t tail = len & 15u;
+  if ((uint32_t)tid < tail) {
+    const uint32_t i = (nchunk << 4) + (uint32_t)tid;
+    dst[i] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(src, goff + i, 0, 0);
+  }
+}
+
+// TILES: 16-column tiles per workgroup.  One batch = NP pairs of blocks.
+template <int TILES>
 __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
-  constexpr int LUT_WORDS = 256 * LUT_COPIES;
-  constexpr int SLOTS = TILES + MAX_RQ;
-  constexpr int RED_WORDS = WAVES * SLOTS * 64 * 4;
-  constexpr int LUT_RED_WORDS = LUT_WORDS > RED_WORDS ? LUT_WORDS : RED_WORDS;
-  // [table / cross-wave sums][per-wave staging of codes and scales]
-  __shared__ __attribute__((aligned(16))) uint32_t smem[LUT_RED_WORDS + WAVES * TILES * (STG_BYTES + STG_SC) / 4];
+  constexpr int NP = TILES <= 3 ? 2 : 1;   // pairs per batch (two keep more bytes in flight)
+  __shared__ __attribute__((aligned(16))) uint32_t lut[LUT_WORDS];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int ROWS = 16 * TILES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
-  const int lrow = lane >> 2, lblk = lane & 3;          // this lane's load: row, block within the batch
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * TILES;
-  const uint32_t K = (uint32_t)p.w.K;
-  const int nbk = (int)(K / 64);
-  const int rq = TIN ? 0 : (p.r + 15) / 16;   // rank tiles computed here
+  const uint32_t K = (uint32_t)p.w.K, RB = K / 2u;   // code bytes per row
+  const int nbk = (int)(K / 64), npair = (nbk + 1) / 2;
+  const uint32_t N = (uint32_t)p.w.N;
+  const uint32_t n0 = blockIdx.x * (uint32_t)ROWS;
+  const uint32_t rows_wg = min((uint32_t)ROWS, N - n0);
+  const int r = p.r;
+  const Lds L = lds_layout(TILES, nbk, r);
 
-  for (int e = tid; e < LUT_WORDS; e += NTHREADS) {
-    const int byte = e / LUT_COPIES;
-    smem[e] = pack_bf16x2(__uint_as_float(kNF4LevelBits[byte & 15]),
-                          __uint_as_float(kNF4LevelBits[byte >> 4]));
+  const auto rX = rsrc(p.X, (uint32_t)p.M * K * 2u);
+  const auto rC = rsrc(p.w.codes, N * RB);
+  const uint32_t nb_all = N * (uint32_t)nbk;
+  const auto rQ = rsrc(p.w.qscale, nb_all);
+  const auto rD = rsrc(p.w.dscale, 4u * ((nb_all + 255u) / 256u));
+  const auto rB = rsrc(p.B, N * (uint32_t)r * 2u);
+
+  // this wave's pairs of blocks, and the per-lane load offsets
+  const int wv = (wave + (int)blockIdx.x) & (WAVES - 1);
+  const int p0 = wv * npair / WAVES, p1 = (wv + 1) * npair / WAVES;
+  uint32_t crow[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) crow[t] = (n0 + 16u * t + (uint32_t)i16) * RB + 16u * (uint32_t)g;
+  const uint32_t koff = 32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1);   // after the swaps
+  const uint32_t xrow = (uint32_t)i16 * K * 2u + 2u * koff;
+
+  struct Batch {
+    u32x4v c[NP][TILES];
+    bf16x8_t x[NP][2][2];
+  };
+  // loads of one (pair u, tile t) slot of a batch; X rides with tile 0
+  auto load_slot = [&](Batch& bt, int pr0, int u, int t) {
+    const int pr = pr0 + u;
+    const bool live = pr < p1;
+    bt.c[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rC, live ? crow[t] + 64u * (uint32_t)pr : OOB, 0, 0);
+    if (t == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = 2 * pr + h;
+        const uint32_t xo = live && kb < nbk ? xrow + 128u * (uint32_t)kb : OOB;
+        bt.x[u][h][0] = ld16(rX, xo);     // rows >= M are past the buffer: zero
+        bt.x[u][h][1] = ld16(rX, xo + 16u);
+      }
+    }
+  };
+  auto load_batch = [&](Batch& bt, int pr0) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u)
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) load_slot(bt, pr0, u, t);
+  };
+
+  Batch cur, nxt;
+  load_batch(cur, p0);
+
+  // ---- tables (their loads queue behind the first batch) ----
+  {
+    // word e holds the pair (byte & 15, byte >> 4) of byte e / 64: thread tid
+    // writes bytes tid/64 + 8i, whose low nibble is tid/64 or tid/64 + 8
+    const float lo0 = __uint_as_float(kNF4LevelBits[tid >> 6]);
+    const float lo1 = __uint_as_float(kNF4LevelBits[(tid >> 6) + 8]);
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, __uint_as_float(kNF4LevelBits[i >> 1]));
+  }
+  float* stab = reinterpret_cast<float*>(smem + L.stab);
+  for (uint32_t e = (uint32_t)tid; e < (uint32_t)ROWS * L.spitch; e += NTHREADS) stab[e] = 0.0f;
+  stage_bytes(smem + L.btab, rB, n0 * (uint32_t)r * 2u, rows_wg * (uint32_t)r * 2u, tid);
+  float* ttab = reinterpret_cast<float*>(smem + L.ttab);
+  {
+    // T = the partials summed in split order (all loads of an element in
+    // flight at once; splits past nsplit read as zero); rows m >= M are zero
+    const auto rP = rsrc(p.tpart, (uint32_t)p.nsplit * 16u * (uint32_t)r * 4u);
+    for (int e = tid; e < 16 * r; e += NTHREADS) {
+      float pv[MAX_SPLIT];
+#pragma unroll
+      for (int sp = 0; sp < MAX_SPLIT; ++sp)
+        pv[sp] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rP, 4u * (uint32_t)(sp * 16 * r + e), 0, 0));
+      float v = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < MAX_SPLIT; ++sp)
+        if (sp < p.nsplit) v += pv[sp];
+      ttab[e] = v;
+      if (blockIdx.x == 0 && e < (int)p.M * r) p.T_save[e] = v;
+    }
+  }
+  __syncthreads();   // the zero fill is done before the scales are written
+  {
+    // restored scales of this workgroup's blocks [q0, q0 + len): 16 per step
+    const uint32_t q0 = n0 * (uint32_t)nbk, len = rows_wg * (uint32_t)nbk;
+    auto fill = [&](uint32_t c, const u32x4v& v, float da, float db, uint32_t ga) {
+      const uint32_t f0 = 16u * c;
+      uint32_t lr = f0 / (uint32_t)nbk, b = f0 - lr * (uint32_t)nbk;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (f0 + k < len) {
+          const float d = ((q0 + f0 + k) >> 8) == ga ? da : db;
+          stab[lr * L.spitch + b] = e4m3_decode((v[k >> 2] >> (8 * (k & 3))) & 127u) * d;
+        }
+        if (++b == (uint32_t)nbk) { b = 0; ++lr; }
+      }
+    };
+    // 16 scale bytes per chunk; a chunk that runs past the workgroup's blocks
+    // is read byte by byte (the qscale array may end there)
+    auto load_q = [&](uint32_t c) -> u32x4v {
+      const uint32_t f0 = 16u * c;
+      if (f0 + 16u <= len) return __builtin_amdgcn_raw_buffer_load_b128(rQ, q0 + f0, 0, 0);
+      u32x4v v = {0u, 0u, 0u, 0u};
+      for (uint32_t k = 0; f0 + k < len; ++k)
+        v[k >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rQ, q0 + f0 + k, 0, 0) << (8 * (k & 3));
+      return v;
+    };
+    auto load_d = [&](uint32_t gi) -> float {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, 4u * gi, 0, 0));
+    };
+    const uint32_t nch = (len + 15u) / 16u;
+    for (uint32_t c0 = (uint32_t)tid; c0 < nch; c0 += 2 * NTHREADS) {
+      const uint32_t c1 = c0 + NTHREADS;
+      const bool two = c1 < nch;
+      const u32x4v v0 = load_q(c0);
+      const u32x4v v1 = two ? load_q(c1) : u32x4v{0u, 0u, 0u, 0u};
+      const uint32_t ga0 = (q0 + 16u * c0) >> 8, gb0 = (q0 + min(16u * c0 + 15u, len - 1u)) >> 8;
+      const uint32_t ga1 = (q0 + 16u * c1) >> 8, gb1 = (q0 + min(16u * c1 + 15u, len - 1u)) >> 8;
+      const float da0 = load_d(ga0), db0 = load_d(gb0);
+      const float da1 = load_d(two ? ga1 : ga0), db1 = load_d(two ? gb1 : gb0);
+      fill(c0, v0, da0, db0, ga0);
+      if (two) fill(c1, v1, da1, db1, ga1);
+    }
   }
   __syncthreads();
 
-  uint8_t* stg = reinterpret_cast<uint8_t*>(smem + LUT_RED_WORDS) +
-                 (size_t)wave * TILES * (STG_BYTES + STG_SC);
-
-  const auto rX = rsrc(p.X, (uint32_t)(p.M * K * 2));
-  const auto rA = rsrc(p.A, (uint32_t)(p.r * K * 2));
-  const auto rC = rsrc(p.w.codes, (uint32_t)(p.w.N * K / 2));
-  const auto rQ = rsrc(p.w.qscale, (uint32_t)(p.w.N * K / 64));
-  const auto rD = rsrc(p.w.dscale, (uint32_t)(4 * ((p.w.N * K / 64 + 255) / 256)));
+  // LDS address of (code byte e of word c, this lane's copy) = byte << 8 | lane * 4,
+  // assembled by one byte permute
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+  auto lookup = [&](uint32_t c, int e) -> uint32_t {
+    const uint32_t addr = __builtin_amdgcn_perm(c, lane4, 0x0C0C0400u + ((uint32_t)e << 8));
+    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lut) + addr);
+  };
 
   f32x4_t acc[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t tacc[MAX_RQ];
-#pragma unroll
-  for (int q = 0; q < MAX_RQ; ++q) tacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int b0 = wave * nbk / WAVES, b1 = (wave + 1) * nbk / WAVES;
-  const uint32_t lut_lane = (uint32_t)(lane & (LUT_COPIES - 1));
-  const uint32_t xoff = (uint32_t)i16 * K * 2 + 32u * g;   // k = 64*blk + 16*g + 8*step + t
-  uint32_t crow[TILES];
+  // multiply batch `bt` (pairs pr0..pr0+NP-1) while the next batch's loads
+  // are issued one slot at a time between the tiles, so that the address
+  // unit works through them while this wave computes
+  auto step = [&](const Batch& bt, Batch& nb, int pr0) {
 #pragma unroll
-  for (int t = 0; t < TILES; ++t) crow[t] = (uint32_t)(n0 + 16 * t + lrow);
-
-  struct Batch { u32x4v c0[TILES], c1[TILES]; uint32_t q[TILES]; float d[TILES]; };
-  auto load_batch = [&](Batch& bt, int bb) {
+    for (int u = 0; u < NP; ++u) {
+      // a pair past the row's end (the last batch of a wave may hold one) has
+      // zero X; any finite scale then adds nothing
+      const int prs = min(pr0 + u, npair - 1);
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const uint32_t blk = (uint32_t)(bb + lblk);
-      const uint32_t off = crow[t] * (K / 2) + 32u * blk;
-      bt.c0[t] = __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0);
-      bt.c1[t] = __builtin_amdgcn_raw_buffer_load_b128(rC, off + 16, 0, 0);
-      const uint32_t qb = crow[t] * (K / 64) + blk;
-      bt.q[t] = __builtin_amdgcn_raw_buffer_load_b8(rQ, qb, 0, 0);
-      bt.d[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, 4 * (qb >> 8), 0, 0));
+      for (int t = 0; t < TILES; ++t) {
+        load_slot(nb, pr0 + NP, u, t);
+        // lower half-wave loaded block 2pr, upper half block 2pr+1: exchange
+        // halves so that words 0,1 hold block 2pr and words 2,3 block 2pr+1
+        const auto s02 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].x, bt.c[u][t].z, false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].y, bt.c[u][t].w, false, false);
+        const uint32_t w[4] = {s02[0], s13[0], s02[1], s13[1]};
+        const f32x2v sc = *reinterpret_cast<const f32x2v*>(stab + (16 * t + i16) * L.spitch + 2 * prs);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4v wa = {lookup(w[2 * h], 0), lookup(w[2 * h], 1), lookup(w[2 * h], 2), lookup(w[2 * h], 3)};
+          const u32x4v wb = {lookup(w[2 * h + 1], 0), lookup(w[2 * h + 1], 1), lookup(w[2 * h + 1], 2),
+                             lookup(w[2 * h + 1], 3)};
+          f32x4_t tmp = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt.x[u][h][0], __builtin_bit_cast(bf16x8_t, wa), tmp, 0, 0, 0);
+          tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt.x[u][h][1], __builtin_bit_cast(bf16x8_t, wb), tmp, 0, 0, 0);
+          const float s = h ? sc.y : sc.x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][e] += s * tmp[e];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  Batch cur, nxt;
-  load_batch(cur, b0);
-  for (int bb = b0; bb < b1; bb += 4) {
-    load_batch(nxt, bb + 4);     // past b1: unused
-    // stage this batch: codes [row][4 blocks x 32 B], scales [row][4 blocks]
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      uint8_t* st = stg + t * (STG_BYTES + STG_SC);
-      *reinterpret_cast<u32x4v*>(st + lrow * STG_PITCH + 32 * lblk) = cur.c0[t];
-      *reinterpret_cast<u32x4v*>(st + lrow * STG_PITCH + 32 * lblk + 16) = cur.c1[t];
-      reinterpret_cast<float*>(st + STG_BYTES)[lrow * 4 + lblk] = e4m3_decode(cur.q[t]) * cur.d[t];
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (bb + j >= b1) break;
-      const uint32_t kb2 = (uint32_t)(bb + j) * 128u;   // byte offset of the block in a bf16 row
-      const bf16x8_t x0 = ld16(rX, xoff + kb2);
-      const bf16x8_t x1 = ld16(rX, xoff + kb2 + 16);
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        const uint8_t* st = stg + t * (STG_BYTES + STG_SC);
-        const u32x2v c = *reinterpret_cast<const u32x2v*>(st + i16 * STG_PITCH + 32 * j + 8 * g);
-        const float sc = reinterpret_cast<const float*>(st + STG_BYTES)[i16 * 4 + j];
-        uint32_t wv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t byte = ((e < 4 ? c.x : c.y) >> (8 * (e & 3))) & 0xFFu;
-          wv[e] = smem[byte * LUT_COPIES + lut_lane];
-        }
-        const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, u32x4v{wv[0], wv[1], wv[2], wv[3]});
-        const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, u32x4v{wv[4], wv[5], wv[6], wv[7]});
-        f32x4_t tmp = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, w0, tmp, 0, 0, 0);
-        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, w1, tmp, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t][e] += sc * tmp[e];
-      }
-#pragma unroll
-      for (int q = 0; q < MAX_RQ; ++q) {
-        if (q < rq) {
-          const uint32_t aoff = (uint32_t)(16 * q + i16) * K * 2 + 32u * g + kb2;
-          tacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, ld16(rA, aoff), tacc[q], 0, 0, 0);
-          tacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, ld16(rA, aoff + 16), tacc[q], 0, 0, 0);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    cur = nxt;
+  // two batches ping-pong (no register copies, which would wait for the
+  // loads); a batch past p1 holds zero X and adds nothing
+  for (int pr = p0; pr < p1; pr += 2 * NP) {
+    step(cur, nxt, pr);
+    step(nxt, cur, pr + NP);
   }
 
   // ---- cross-wave sums (fixed wave order), LoRA term, store ----
-  __syncthreads();   // the table is no longer read
-  float* red = reinterpret_cast<float*>(smem);
+  __syncthreads();   // every wave is done with the scale table
+  float* red = reinterpret_cast<float*>(smem + L.red);
+  // slot layout [wave][tile][m][16]; lane (col i16, rows 4g..4g+3)
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[((wave * SLOTS + t) * 64 + lane) * 4 + e] = acc[t][e];
-#pragma unroll
-  for (int q = 0; q < MAX_RQ; ++q)
-    if (q < rq)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[((wave * SLOTS + TILES + q) * 64 + lane) * 4 + e] = tacc[q][e];
+    for (int e = 0; e < 4; ++e) red[((wave * TILES + t) * 16 + 4 * g + e) * 16 + i16] = acc[t][e];
   __syncthreads();
-
-  // the value of output (m, col) of slot `sl` sits in lane 16*(m/4) + col, element m%4
-  auto total = [&](int sl, int m, int col) {
-    const int idx = (16 * (m >> 2) + col) * 4 + (m & 3);
-    float v = 0.0f;
+  const u16* btab = reinterpret_cast<const u16*>(smem + L.btab);
+  constexpr int COLS = 16 * TILES;
+  for (int e = tid; e < (int)p.M * COLS; e += NTHREADS) {
+    const int m = e / COLS, c = e - m * COLS;
+    if ((uint32_t)c < rows_wg) {
+      float base = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[(w * SLOTS + sl) * 64 * 4 + idx];
-    return v;
-  };
-
-  auto t_at = [&](int m, int j) -> float {
-    if constexpr (TIN) return p.T_save[m * p.r + j];
-    else return total(TILES + j / 16, m, j % 16);
-  };
-  if (!TIN && blockIdx.x == 0) {
-    for (int e = tid; e < 16 * p.r; e += NTHREADS) {
-      const int m = e / p.r, j = e % p.r;
-      if (m < p.M) p.T_save[m * p.r + j] = total(TILES + j / 16, m, j % 16);
-    }
-  }
-  for (int e = tid; e < 256 * TILES; e += NTHREADS) {
-    const int m = e / (16 * TILES), c = e % (16 * TILES);
-    const int64_t nn = n0 + c;
-    if (m < p.M && nn < p.w.N) {
+      for (int w = 0; w < WAVES; ++w) base += red[((w * TILES + (c >> 4)) * 16 + m) * 16 + (c & 15)];
       float lora = 0.0f;
-      for (int j = 0; j < p.r; ++j) lora += t_at(m, j) * bf16_to_f32(p.B[nn * p.r + j]);
-      p.Y[m * p.w.N + nn] = f32_to_bf16(total(c / 16, m, c % 16) + p.s * lora);
+      if ((r & 7) == 0) {      // 8 terms per step from 16-byte LDS reads, in j order
+        const f32x4_t* tv = reinterpret_cast<const f32x4_t*>(ttab + m * r);
+        const u32x4v* bv = reinterpret_cast<const u32x4v*>(btab + c * r);
+#pragma unroll 2
+        for (int j8 = 0; j8 < r / 8; ++j8) {
+          const f32x4_t t0 = tv[2 * j8], t1 = tv[2 * j8 + 1];
+          const u32x4v b = bv[j8];
+          const float bw[8] = {__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                               __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u),
+                               __uint_as_float(b.z << 16), __uint_as_float(b.z & 0xFFFF0000u),
+                               __uint_as_float(b.w << 16), __uint_as_float(b.w & 0xFFFF0000u)};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) lora += t0[k] * bw[k];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) lora += t1[k] * bw[4 + k];
+        }
+      } else {
+        for (int j = 0; j < r; ++j) lora += ttab[m * r + j] * bf16_to_f32(btab[c * r + j]);
+      }
+      p.Y[(size_t)m * N + n0 + c] = f32_to_bf16(base + p.s * lora);
     }
   }
+}
+
+template <int TILES>
+static hipError_t launch_one(const DecArgs& p, hipStream_t st) {
+  const int nbk = (int)(p.w.K / 64);
+  const Lds L = lds_layout(TILES, nbk, p.r);
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<TILES>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)MAX_DYN_LDS);
+  });
+  if (attr != hipSuccess) return attr;
+  const unsigned grid = (unsigned)((p.w.N + 16 * TILES - 1) / (16 * TILES));
+  hipLaunchKernelGGL((k_decode<TILES>), dim3(grid), dim3(NTHREADS), L.total, st, p);
+  return hipGetLastError();
+}
+
+static int device_cus() {
+  static int cus = 0;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  });
+  return cus;
+}
+
+// tiles per workgroup: the fewest that keep the grid within one workgroup per
+// compute unit (more tiles per workgroup share each X fragment more widely)
+static int pick_tiles(int64_t N, int64_t K, int r) {
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t cus = device_cus();
+  int t = (int)std::min<int64_t>(MAX_TILES, std::max<int64_t>(1, (tiles + cus - 1) / cus));
+  while (t > 1 && lds_layout(t, (int)(K / 64), r).total > MAX_DYN_LDS) --t;
+  return t;
+}
+
+// Split of the contraction for the T partials: chunks of at least 512 (a
+// multiple of 64), at most MAX_SPLIT of them.
+struct TSplit {
+  int nsplit;
+  uint32_t kchunk;
+};
+static TSplit t_split(int64_t K) {
+  int64_t chunk = std::max<int64_t>(512, (K + MAX_SPLIT - 1) / MAX_SPLIT);
+  chunk = (chunk + 63) / 64 * 64;
+  TSplit s;
+  s.kchunk = (uint32_t)chunk;
+  s.nsplit = (int)((K + chunk - 1) / chunk);
+  return s;
 }
 
 }  // namespace dec
 
-bool decode_fits(int64_t M, const NF4View& w, int r) {
-  const int64_t lim = (int64_t)1 << 31;
-  return M <= 16 && w.N * w.K / 2 < lim && 16 * w.K * 2 < lim && (int64_t)r * w.K * 2 < lim;
+int64_t decode_workspace_elems(int64_t K, int r) {
+  return (int64_t)dec::t_split(K).nsplit * 16 * r;
 }
 
-template <bool TIN>
-static void launch_tiles(const dec::DecArgs& p, int64_t N, hipStream_t st) {
-  // as many 16-column tiles per workgroup as keeps at least 256 workgroups
-  if (N >= 64 * 256)
-    hipLaunchKernelGGL((dec::k_decode<4, TIN>), dim3((unsigned)((N + 63) / 64)), dim3(dec::NTHREADS),
-                       0, st, p);
-  else if (N >= 32 * 256)
-    hipLaunchKernelGGL((dec::k_decode<2, TIN>), dim3((unsigned)((N + 31) / 32)), dim3(dec::NTHREADS),
-                       0, st, p);
-  else
-    hipLaunchKernelGGL((dec::k_decode<1, TIN>), dim3((unsigned)((N + 15) / 16)), dim3(dec::NTHREADS),
-                       0, st, p);
+bool decode_fits(int64_t M, const NF4View& w, int r) {
+  const int64_t lim = (int64_t)1 << 31;
+  if (!(M >= 1 && M <= 16 && w.N * w.K / 2 < lim && 16 * w.K * 2 < lim && (int64_t)r * w.K * 2 < lim &&
+        w.N * r * 2 < lim))
+    return false;
+  return dec::lds_layout(1, (int)(w.K / 64), r).total <= dec::MAX_DYN_LDS;
 }
 
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st) {
-  dec::DecArgs p;
-  p.X = X; p.M = M; p.w = w; p.A = A; p.B = B; p.r = r; p.s = s; p.Y = Y; p.T_save = T_save;
-  if (r <= 16 * dec::MAX_RQ) {           // T computed inside, from the same X fragments
-    launch_tiles<false>(p, w.N, st);
-    return hipGetLastError();
-  }
-  hipError_t e = launch_lora_down(X, A, M, w.K, r, ws, T_save, st);
+  const dec::TSplit ts = dec::t_split(w.K);
+  hipLaunchKernelGGL(dec::k_tpart, dim3((unsigned)((r + 15) / 16), (unsigned)ts.nsplit), dim3(64 * dec::TP_WAVES),
+                     0, st, X, (int)M, (uint32_t)w.K, A, r, ts.kchunk, ws);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_tiles<true>(p, w.N, st);
-  return hipGetLastError();
+  dec::DecArgs p;
+  p.X = X; p.M = M; p.w = w; p.B = B; p.r = r; p.s = s; p.tpart = ws; p.nsplit = ts.nsplit;
+  p.Y = Y; p.T_save = T_save;
+  switch (dec::pick_tiles(w.N, w.K, r)) {
+    case 1: return dec::launch_one<1>(p, st);
+    case 2: return dec::launch_one<2>(p, st);
+    case 3: return dec::launch_one<3>(p, st);
+    case 4: return dec::launch_one<4>(p, st);
+    case 5: return dec::launch_one<5>(p, st);
+    case 6: return dec::launch_one<6>(p, st);
+    case 7: return dec::launch_one<7>(p, st);
+    default: return dec::launch_one<8>(p, st);
+  }
 }
 
 }  // namespace qln

@@ -143,6 +143,38 @@ def test_fwd_bwd_small(orc, N, K, M, r, alpha):
     assert_close(tensor_f64(dB), dBr, "dB")
 
 
+# decode-size forwards (M <= 16): the HBM-streaming kernel with every tile
+# count, in-kernel and precomputed T, ragged column tiles and uneven splits of
+# the contraction over the waves
+DECODE = [
+    # N, K, M, r, alpha
+    (1000, 512, 3, 8, 16.0),        # one block per wave, ragged last tile
+    (4100, 2304, 7, 64, 16.0),      # T precomputed; 36 blocks over 8 waves
+    (50, 768, 16, 128, 8.0),        # maximum rank, fewer rows than one tile
+    (2048, 11008, 16, 32, 32.0),    # two rank tiles of T in-kernel; K % 256 != 0
+    (28672, 1024, 1, 16, 32.0),     # seven column tiles per workgroup
+    (40000, 256, 4, 24, 16.0),      # eight tiles per workgroup, more than one round
+    (12000, 4096, 16, 16, 32.0),    # three tiles per workgroup
+]
+
+
+@pytest.mark.parametrize("N,K,M,r,alpha", DECODE)
+def test_decode_fwd_small(orc, N, K, M, r, alpha):
+    cfg = si.custom(N=N, K=K, M=M, r=r, alpha=alpha, seed=3 * N + K)
+    lay = GpuLayer(cfg)
+    log(f"[decode fwd] N={N} K={K} M={M} r={r}")
+    Y, T = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, lay.dB_in, alpha)
+    Y2, T2 = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, lay.dB_in, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), "run-to-run"
+    assert torch.equal(T, T2), "run-to-run T"
+    codes, qs, ds = _quant_host(lay.w)
+    Wdq = orc.nf4_dequantize(codes, qs, ds, N, K)
+    Yr, Tr = orc.qlora_fwd(Wdq, lay.X, lay.A, lay.B, alpha)
+    assert_close(tensor_f64(T), Tr, "T")
+    assert_close(tensor_f64(Y), Yr, "Y")
+
+
 def test_zero_B_gives_bitwise_base_output(orc):
     cfg = si.custom(N=384, K=512, M=100, r=16, alpha=32.0, seed=3)
     lay = GpuLayer(cfg)
