@@ -43,6 +43,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "device.h"
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   // multiply batch `bt` (pairs pr0..pr0+NP-1) while the next batch's loads
   // are issued one slot at a time between the tiles, so that the address
   // unit works through them while this wave computes
-  auto step = [&](const Batch& bt, Batch& nb, int pr0) {
+  auto step = [&](const Batch& bt, Batch& nb, int pr0, auto prefetch) {
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       // a pair past the row's end (the last batch of a wave may hold one) has
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       const int prs = min(pr0 + u, npair - 1);
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
-        load_slot(nb, pr0 + NP, u, t);
+        if constexpr (decltype(prefetch)::value) load_slot(nb, pr0 + NP, u, t);
         // lower half-wave loaded block 2pr, upper half block 2pr+1: exchange
         // halves so that words 0,1 hold block 2pr and words 2,3 block 2pr+1
         const auto s02 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].x, bt.c[u][t].z, false, false);
@@ -359,10 +360,20 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   };
 
   // two batches ping-pong (no register copies, which would wait for the
-  // loads); a batch past p1 holds zero X and adds nothing
-  for (int pr = p0; pr < p1; pr += 2 * NP) {
-    step(cur, nxt, pr);
-    step(nxt, cur, pr + NP);
+  // loads); the tail issues no loads past this wave's last pair, since even a
+  // load that returns zero costs address-unit time
+  const std::integral_constant<bool, true> pf;
+  const std::integral_constant<bool, false> nopf;
+  int pr = p0;
+  for (; pr + 2 * NP < p1; pr += 2 * NP) {
+    step(cur, nxt, pr, pf);
+    step(nxt, cur, pr + NP, pf);
+  }
+  if (pr + NP < p1) {
+    step(cur, nxt, pr, pf);
+    step(nxt, cur, pr + NP, nopf);
+  } else if (pr < p1) {
+    step(cur, nxt, pr, nopf);
   }
 
   // ---- cross-wave sums (fixed wave order), LoRA term, store ----
