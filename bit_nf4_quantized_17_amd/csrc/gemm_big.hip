@@ -303,16 +303,35 @@ __device__ __forceinline__ void frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], cons
   for (int b = 0; b < 4; ++b) fb[b] = read_b<MODE>(sB, wn, b, ks, lane);
 }
 
+// Loads of the stage after next are woven in too: an A row pair is reloaded
+// right after it is stored, the weight block's scale bytes right after its
+// table is built and its codes once they are dequantized, so the per-CU
+// address unit sees a steady trickle instead of one burst per step.
+struct NextLoads {
+  const Bufs* bf;
+  uint32_t a_base, a_step, a_c0;   // A stage to load into ra (contraction start)
+  uint32_t wn, wk, K;              // weight block to load into w
+  bool wlive;
+};
+
 template <int MODE>
 __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][4], const u16* sA,
                                                const u16* sB, int wm, int wn, int lane,
-                                               const StageA& ra, const StageW& w,
-                                               u16* sA_next, u16* wdst_next, int tid) {
+                                               StageA& ra, StageW& w,
+                                               u16* sA_next, u16* wdst_next, int tid,
+                                               const NextLoads& nl) {
   bf16x8_t fa[2][4], fb[2][4];
   frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
   const Table t = make_table(stage_scale(w));
   const uint32_t c[8] = {w.c[0].x, w.c[0].y, w.c[0].z, w.c[0].w,
                          w.c[1].x, w.c[1].y, w.c[1].z, w.c[1].w};
+  {
+    // the scale byte and group constant of the weight block after next
+    const uint32_t blk = nl.wn * (nl.K / 64) + nl.wk / 64;
+    w.q = __builtin_amdgcn_raw_buffer_load_b8(nl.bf->qscale, blk, 0, 0);
+    w.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        nl.bf->dscale, nl.wlive ? 4 * (blk >> 8) : 0xFFFFFFF0u, 0, 0));
+  }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int cur = ks & 1;
@@ -330,7 +349,10 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][4], const u16*
       dequant8(t, c[i], o);
       *reinterpret_cast<uint4*>(wdst_next + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(sA_next + (tid / 8 + 32 * i) * APITCH + (tid % 8) * 8) = ra.v[i];
+      ra.v[i] = bload16(nl.bf->a, nl.a_base + i * nl.a_step + 2 * nl.a_c0);
     }
+    if (ks == 1) w.c[0] = bload16(nl.bf->codes, nl.wn * (nl.K / 2) + nl.wk / 2);
+    if (ks == 3) w.c[1] = bload16(nl.bf->codes, nl.wn * (nl.K / 2) + nl.wk / 2 + 16);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -409,14 +431,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   // compiler keep two copies of the accumulators)
   for (int64_t kt = 0; kt < nk; kt += 2) {
     // buffer 0 holds stage kt; ra = A(kt+1), w1 = W(kt+1), w0 = W(kt+2)
-    step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid);
-    load_a(ra, bf, a_base, a_step, (uint32_t)((kt + 2) * BK));
-    load_w(w1, bf, w_n(kt + 3), w_k(kt + 3), K, kt + 3 < nk);
+    {
+      const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 2) * BK), w_n(kt + 3), w_k(kt + 3), K,
+                         kt + 3 < nk};
+      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl);
+    }
     __syncthreads();
     // buffer 1 holds stage kt+1; ra = A(kt+2), w0 = W(kt+2), w1 = W(kt+3)
-    step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid);
-    load_a(ra, bf, a_base, a_step, (uint32_t)((kt + 3) * BK));
-    load_w(w0, bf, w_n(kt + 4), w_k(kt + 4), K, kt + 4 < nk);
+    {
+      const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 3) * BK), w_n(kt + 4), w_k(kt + 4), K,
+                         kt + 4 < nk};
+      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl);
+    }
     __syncthreads();
   }
 
