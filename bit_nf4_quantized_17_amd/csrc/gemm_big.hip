@@ -11,12 +11,14 @@
 // QLoRA works": dequantize NF4 to bfloat16 right before the matrix product,
 // gradients flow through the dequantized weights.
 //
-// Tiling (gfx950): 256 threads = 4 waves, output tile 256 x 256, contraction
-// step 64.  Each wave owns a 128 x 128 quarter as 4 x 4 accumulators of
-// v_mfma_f32_32x32x16_bf16 (256 accumulator registers).  LDS holds two stages
+// Tiling (gfx950): 512 threads = 8 waves (two per SIMD, so one wave's MFMAs
+// overlap the other's dequantization), output tile 256 x 256, contraction
+// step 64.  Each wave owns a 128 x 64 eighth as 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16 (128 accumulator registers).  LDS holds two stages
 // of both operand tiles (about 144 KiB); global loads run two stages ahead in
 // registers, so one barrier per step separates writing stage k+1 from
-// reading stage k.  The forward's weight tile is [n][k] (contraction
+// reading stage k.  A thread produces a quarter of an A-tile column chunk and
+// half of one 64-code weight block per step.  The forward's weight tile is [n][k] (contraction
 // contiguous: plain 16-byte fragment reads); the backward's is [n][k] with
 // n the contraction, read with ds_read_b64_tr_b16 (within each 16-lane group
 // lane i receives element i%4 of the rows addressed by lanes 4j + i/4, which
@@ -40,7 +42,7 @@ constexpr int TPITCH = BN + 16;         // backward W tile [64 n][272] (544-byte
 constexpr int A_ELEMS = BM * APITCH;    // 18432
 constexpr int BF_ELEMS = BN * FPITCH;   // 18432
 constexpr int BT_ELEMS = BK * TPITCH;   // 17408
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 512;
 
 enum { MODE_FWD = 0, MODE_DX = 1 };
 
@@ -136,25 +138,23 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-struct StageA { uint4 v[8]; };           // A tile: 8 x 16 bytes per thread
-struct StageW { uint4 c[2]; uint32_t q; float d; };  // codes, raw scale byte, group constant
+struct StageA { uint4 v[4]; };                    // A tile: 4 x 16 bytes per thread
+struct StageW { uint4 c; uint32_t q; float d; };  // half a block's codes, raw scale byte, group constant
 
-// A tile rows m0 + tid/8 + 32q, contraction c0 + 8*(tid%8) .. +8
+// A tile rows m0 + tid/8 + 64q, contraction c0 + 8*(tid%8) .. +8
 __device__ __forceinline__ void load_a(StageA& st, const Bufs& b, uint32_t row_off0,
                                        uint32_t row_step, uint32_t c0) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) st.v[q] = bload16(b.a, row_off0 + q * row_step + 2 * c0);
+  for (int q = 0; q < 4; ++q) st.v[q] = bload16(b.a, row_off0 + q * row_step + 2 * c0);
 }
 
-// the thread's weight block: row n, columns k .. k+63.  The scale is decoded
-// only when the block is dequantized (one step later), so nothing waits for
-// these loads now; a stage past the last one (live == false) gets group
-// constant 0, so it multiplies as a zero tile.
-__device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, uint32_t k,
+// the thread's half block: row n, columns k + 32*half .. +32.  The scale is
+// decoded only when the block is dequantized (one step later), so nothing
+// waits for these loads now; a stage past the last one (live == false) gets
+// group constant 0, so it multiplies as a zero tile.
+__device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, uint32_t k, uint32_t half,
                                        uint32_t K, bool live) {
-  const uint32_t off = n * (K / 2) + k / 2;
-  st.c[0] = bload16(b.codes, off);
-  st.c[1] = bload16(b.codes, off + 16);
+  st.c = bload16(b.codes, n * (K / 2) + k / 2 + 16 * half);
   const uint32_t blk = n * (K / 64) + k / 64;
   st.q = __builtin_amdgcn_raw_buffer_load_b8(b.qscale, blk, 0, 0);
   // a dead stage reads past the end of the group constants, which returns 0
@@ -166,8 +166,8 @@ __device__ __forceinline__ float stage_scale(const StageW& st) { return e4m3_dec
 
 __device__ __forceinline__ void store_a(const StageA& st, u16* sA, int tid) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    *reinterpret_cast<uint4*>(sA + (tid / 8 + 32 * q) * APITCH + (tid % 8) * 8) = st.v[q];
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<uint4*>(sA + (tid / 8 + 64 * q) * APITCH + (tid % 8) * 8) = st.v[q];
 }
 
 // LoRA prologue A-side tile: s times fp32 T or U, rounded to bf16 (guarded loads)
@@ -175,8 +175,8 @@ __device__ __forceinline__ void lora_a_tile(const float* src, int64_t ld, int64_
                                             int64_t C, int64_t m0, int64_t c0, bool vec,
                                             float s, u16* sA, int tid) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int64_t row = m0 + tid / 8 + 32 * q;
+  for (int q = 0; q < 4; ++q) {
+    const int64_t row = m0 + tid / 8 + 64 * q;
     const int64_t c = c0 + (tid % 8) * 8;
     float x[8];
     if (row < rows && c + 8 <= C && vec) {
@@ -189,46 +189,49 @@ __device__ __forceinline__ void lora_a_tile(const float* src, int64_t ld, int64_
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= s;
-    *reinterpret_cast<uint4*>(sA + (tid / 8 + 32 * q) * APITCH + (tid % 8) * 8) =
+    *reinterpret_cast<uint4*>(sA + (tid / 8 + 64 * q) * APITCH + (tid % 8) * 8) =
         make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                    pack_bf16x2(x[6], x[7]));
   }
 }
 
-// dequantize the thread's block and store its 64 bf16 values contiguously at dst
+// where the thread's 32 dequantized values go: forward tile [256 n][FPITCH],
+// block row tid/2; backward tile [64 n][TPITCH], block (tid/2) = 4 per row
+template <int MODE>
+__device__ __forceinline__ u16* w_dst(u16* sB, int tid) {
+  const int blk = tid >> 1, half = tid & 1;
+  if constexpr (MODE == MODE_FWD) return sB + blk * FPITCH + 32 * half;
+  else return sB + (blk >> 2) * TPITCH + 64 * (blk & 3) + 32 * half;
+}
+
+// dequantize the thread's half block and store its 32 bf16 values at dst
 __device__ __forceinline__ void store_w(const StageW& st, u16* dst) {
   const Table t = make_table(stage_scale(st));
-  const uint32_t c[8] = {st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w,
-                         st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w};
+  const uint32_t c[4] = {st.c.x, st.c.y, st.c.z, st.c.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     uint32_t o[4];
     dequant8(t, c[i], o);
     *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
-template <int MODE>
-__device__ __forceinline__ u16* w_dst(u16* sB, int tid) {
-  if constexpr (MODE == MODE_FWD) return sB + tid * FPITCH;
-  else return sB + (tid / 4) * TPITCH + 64 * (tid % 4);
-}
-
-// LoRA prologue operand of the B side, bf16: forward B [J][r] rows n0 + tid
-// (one 64-wide chunk of r); backward A [r][J] rows c0 + tid/4, columns
-// j0 + 64*(tid%4) .. +64.  Written in the same LDS layout as the weight tile.
+// LoRA prologue operand of the B side, bf16, in the weight tile's layout:
+// forward B [J][r] row j0 + tid/2, columns c0 + 32*(tid%2) .. +32; backward
+// A [r][J] row c0 + (tid/2)/4, columns j0 + 64*((tid/2)%4) + 32*(tid%2) .. +32.
 template <int MODE>
 __device__ __forceinline__ void lora_b_tile(const BigArgs& p, u16* sB, int64_t j0, int64_t c0,
                                             int tid) {
   u16* dst = w_dst<MODE>(sB, tid);
+  const int blk = tid >> 1, half = tid & 1;
   int64_t row, col0, rows, cols, ld;
   if constexpr (MODE == MODE_FWD) {
-    row = j0 + tid; col0 = c0; rows = p.J; cols = p.r; ld = p.r;
+    row = j0 + blk; col0 = c0 + 32 * half; rows = p.J; cols = p.r; ld = p.r;
   } else {
-    row = c0 + tid / 4; col0 = j0 + 64 * (tid % 4); rows = p.r; cols = p.J; ld = p.J;
+    row = c0 + (blk >> 2); col0 = j0 + 64 * (blk & 3) + 32 * half; rows = p.r; cols = p.J; ld = p.J;
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < 4; ++q) {
     const int64_t c = col0 + 8 * q;
     uint32_t v[4] = {0, 0, 0, 0};
     if (row < rows && c + 8 <= cols && p.lb_vec) {
@@ -244,16 +247,17 @@ __device__ __forceinline__ void lora_b_tile(const BigArgs& p, u16* sB, int64_t j
 }
 
 // ---------------------------------------------------------------------------
-// MFMA on one LDS stage
+// MFMA on one LDS stage: wave (wm, wn) owns rows wm*128 .. +128 and columns
+// wn*64 .. +64 of the tile
 // ---------------------------------------------------------------------------
 template <int MODE>
 __device__ __forceinline__ bf16x8_t read_b(const u16* sB, int wn, int b, int ks, int lane) {
   if constexpr (MODE == MODE_FWD) {
     return *reinterpret_cast<const bf16x8_t*>(
-        sB + (wn * 128 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + (lane >> 5) * 8);
+        sB + (wn * 64 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + (lane >> 5) * 8);
   } else {
     const int L = lane & 15;
-    const int col = wn * 128 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+    const int col = wn * 64 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
     const int row = ks * 16 + 8 * (lane >> 5) + (L >> 2);
     const lds_short* base = (const lds_short*)(sB);
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -267,64 +271,56 @@ __device__ __forceinline__ bf16x8_t read_b(const u16* sB, int wn, int b, int ks,
 }
 
 template <int MODE>
-__device__ __forceinline__ void mma_stage(f32x16_t (&acc)[4][4], const u16* sA, const u16* sB,
-                                          int wm, int wn, int lane) {
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8_t fa[4], fb[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      fa[a] = *reinterpret_cast<const bf16x8_t*>(
-          sA + (wm * 128 + a * 32 + (lane & 31)) * APITCH + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) fb[b] = read_b<MODE>(sB, wn, b, ks, lane);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
-  }
-}
-
-// One contraction step with the producer work for the next stage woven in:
-// for each 16-wide substep ks, the fragments of ks+1 are read while the 16
-// MFMAs of ks issue, then a quarter of the next stage is written to the other
-// LDS buffer (two 16-byte A rows and 16 dequantized weights).  Scheduling
-// barriers keep the compiler from hoisting all fragment reads of the stage
-// (128 registers) ahead of the MFMAs.
-template <int MODE>
-__device__ __forceinline__ void frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], const u16* sA,
+__device__ __forceinline__ void frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[2], const u16* sA,
                                       const u16* sB, int wm, int wn, int ks, int lane) {
 #pragma unroll
   for (int a = 0; a < 4; ++a)
     fa[a] = *reinterpret_cast<const bf16x8_t*>(
         sA + (wm * 128 + a * 32 + (lane & 31)) * APITCH + ks * 16 + (lane >> 5) * 8);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) fb[b] = read_b<MODE>(sB, wn, b, ks, lane);
+  for (int b = 0; b < 2; ++b) fb[b] = read_b<MODE>(sB, wn, b, ks, lane);
 }
 
-// Loads of the stage after next are woven in too: an A row pair is reloaded
-// right after it is stored, the weight block's scale bytes right after its
-// table is built and its codes once they are dequantized, so the per-CU
-// address unit sees a steady trickle instead of one burst per step.
+template <int MODE>
+__device__ __forceinline__ void mma_stage(f32x16_t (&acc)[4][2], const u16* sA, const u16* sB,
+                                          int wm, int wn, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    bf16x8_t fa[4], fb[2];
+    frags<MODE>(fa, fb, sA, sB, wm, wn, ks, lane);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+  }
+}
+
+// One contraction step with the producer work for the next stage woven in:
+// for each 16-wide substep ks, the fragments of ks+1 are read while the 8
+// MFMAs of ks issue, then a quarter of the next stage is written to the other
+// LDS buffer (one 16-byte A chunk and 8 dequantized weights).  Loads of the
+// stage after next are woven in too: the A chunk is reloaded right after it
+// is stored, the weight block's scale bytes right after its table is built
+// and its codes once they are dequantized, so the per-CU address unit sees a
+// steady trickle instead of one burst per step.
 struct NextLoads {
   const Bufs* bf;
   uint32_t a_base, a_step, a_c0;   // A stage to load into ra (contraction start)
-  uint32_t wn, wk, K;              // weight block to load into w
+  uint32_t wn, wk, whalf, K;       // weight half block to load into w
   bool wlive;
 };
 
 template <int MODE>
-__device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][4], const u16* sA,
+__device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16* sA,
                                                const u16* sB, int wm, int wn, int lane,
                                                StageA& ra, StageW& w,
                                                u16* sA_next, u16* wdst_next, int tid,
                                                const NextLoads& nl) {
-  bf16x8_t fa[2][4], fb[2][4];
+  bf16x8_t fa[2][4], fb[2][2];
   frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
   const Table t = make_table(stage_scale(w));
-  const uint32_t c[8] = {w.c[0].x, w.c[0].y, w.c[0].z, w.c[0].w,
-                         w.c[1].x, w.c[1].y, w.c[1].z, w.c[1].w};
+  const uint32_t c[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
   {
     // the scale byte and group constant of the weight block after next
     const uint32_t blk = nl.wn * (nl.K / 64) + nl.wk / 64;
@@ -339,20 +335,28 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][4], const u16*
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 2; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b],
                                                             0, 0, 0);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = 2 * ks + h;
+    {
       uint32_t o[4];
-      dequant8(t, c[i], o);
-      *reinterpret_cast<uint4*>(wdst_next + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(sA_next + (tid / 8 + 32 * i) * APITCH + (tid % 8) * 8) = ra.v[i];
-      ra.v[i] = bload16(nl.bf->a, nl.a_base + i * nl.a_step + 2 * nl.a_c0);
+      dequant8(t, c[ks], o);
+      *reinterpret_cast<uint4*>(wdst_next + 8 * ks) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(sA_next + (tid / 8 + 64 * ks) * APITCH + (tid % 8) * 8) = ra.v[ks];
+      ra.v[ks] = bload16(nl.bf->a, nl.a_base + ks * nl.a_step + 2 * nl.a_c0);
     }
-    if (ks == 1) w.c[0] = bload16(nl.bf->codes, nl.wn * (nl.K / 2) + nl.wk / 2);
-    if (ks == 3) w.c[1] = bload16(nl.bf->codes, nl.wn * (nl.K / 2) + nl.wk / 2 + 16);
+    if (ks == 3) w.c = bload16(nl.bf->codes, nl.wn * (nl.K / 2) + nl.wk / 2 + 16 * nl.whalf);
+#ifndef QLN_NO_INTERLEAVE
+    // keep the dequantization's VALU work between the MFMAs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // next fragments
+      else if (i < 7) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);             // LDS stores
+      else __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                         // global loads
+    }
+#endif
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -367,15 +371,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   u16* sB[2] = {smem + 2 * A_ELEMS, smem + 2 * A_ELEMS + b_elems<MODE>()};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t m0 = (int64_t)blockIdx.x * BM;
   const int64_t j0 = (int64_t)blockIdx.y * BN;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
@@ -400,17 +404,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   bf.qscale = rsrc(p.w.qscale, (uint32_t)(p.w.N * p.w.K / 64));
   bf.dscale = rsrc(p.w.dscale, (uint32_t)(4 * ((p.w.N * p.w.K / 64 + 255) / 256)));
   const uint32_t K = (uint32_t)p.w.K;
-  const uint32_t a_row0 = (uint32_t)((m0 + tid / 8) * p.lda * 2) + 2 * 8 * (tid % 8);
-  const uint32_t a_step = (uint32_t)(32 * p.lda * 2);
-  const uint32_t a_base = a_row0;   // rows past M give offsets past the end (host checks 32-bit room)
+  // rows past M give offsets past the end (the host checks 32-bit room)
+  const uint32_t a_base = (uint32_t)((m0 + tid / 8) * p.lda * 2) + 2 * 8 * (tid % 8);
+  const uint32_t a_step = (uint32_t)(64 * p.lda * 2);
+  const int wblk = tid >> 1;
+  const uint32_t whalf = (uint32_t)(tid & 1);
   // weight block coordinates of this thread for contraction step kt
   auto w_n = [&](int64_t kt) -> uint32_t {
-    if constexpr (MODE == MODE_FWD) return (uint32_t)(j0 + tid);
-    else return (uint32_t)(kt * BK + tid / 4);
+    if constexpr (MODE == MODE_FWD) return (uint32_t)(j0 + wblk);
+    else return (uint32_t)(kt * BK + (wblk >> 2));
   };
   auto w_k = [&](int64_t kt) -> uint32_t {
     if constexpr (MODE == MODE_FWD) return (uint32_t)(kt * BK);
-    else return (uint32_t)(j0 + 64 * (tid % 4));
+    else return (uint32_t)(j0 + 64 * (wblk & 3));
   };
   u16* wdst0 = w_dst<MODE>(sB[0], tid);
   u16* wdst1 = w_dst<MODE>(sB[1], tid);
@@ -419,12 +425,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   StageA ra;
   StageW w0, w1;
   load_a(ra, bf, a_base, a_step, 0);
-  load_w(w0, bf, w_n(0), w_k(0), K, true);
+  load_w(w0, bf, w_n(0), w_k(0), whalf, K, true);
   store_a(ra, sA[0], tid);
   store_w(w0, wdst0);
   load_a(ra, bf, a_base, a_step, BK);
-  load_w(w1, bf, w_n(1), w_k(1), K, 1 < nk);
-  load_w(w0, bf, w_n(2), w_k(2), K, 2 < nk);
+  load_w(w1, bf, w_n(1), w_k(1), whalf, K, 1 < nk);
+  load_w(w0, bf, w_n(2), w_k(2), whalf, K, 2 < nk);
   __syncthreads();
   // steps are taken in pairs; with an odd count the last pair's second step
   // multiplies a zero weight tile (no early exit: that would make the
@@ -432,14 +438,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   for (int64_t kt = 0; kt < nk; kt += 2) {
     // buffer 0 holds stage kt; ra = A(kt+1), w1 = W(kt+1), w0 = W(kt+2)
     {
-      const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 2) * BK), w_n(kt + 3), w_k(kt + 3), K,
+      const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 2) * BK), w_n(kt + 3), w_k(kt + 3), whalf, K,
                          kt + 3 < nk};
       step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl);
     }
     __syncthreads();
     // buffer 1 holds stage kt+1; ra = A(kt+2), w0 = W(kt+2), w1 = W(kt+3)
     {
-      const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 3) * BK), w_n(kt + 4), w_k(kt + 4), K,
+      const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 3) * BK), w_n(kt + 4), w_k(kt + 4), whalf, K,
                          kt + 4 < nk};
       step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl);
     }
@@ -450,8 +456,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + wn * 128 + b * 32 + (lane & 31);
+    for (int b = 0; b < 2; ++b) {
+      const int64_t j = j0 + wn * 64 + b * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t i = m0 + wm * 128 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
