@@ -42,7 +42,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
+#include <random>
 #include <type_traits>
 
 #include "common.h"
@@ -54,7 +56,7 @@ namespace dec {
 constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
 constexpr int LUT_WORDS = 256 * 64;                   // one copy per lane, 64 KB (static LDS)
-constexpr uint32_t MAX_DYN_LDS = 96u * 1024u;         // what is left of the 160 KB
+constexpr uint32_t MAX_DYN_LDS = 95u * 1024u;         // what is left of the 160 KB (1 KB for small statics)
 constexpr int MAX_TILES = 8;
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every range this path uses
 constexpr int TP_WAVES = 4;             // waves of a k_tpart workgroup
@@ -66,8 +68,11 @@ typedef float f32x2v __attribute__((ext_vector_type(2)));
 struct DecArgs {
   const u16* X; int64_t M;          // X [M][K], M <= 16
   NF4View w;                        // W [N][K]
-  const u16* B; int r; float s;
-  const float* tpart; int nsplit;   // T partial sums [nsplit][16][r]
+  const u16* A; const u16* B; int r; float s;
+  float* tpart; int nsplit;         // T partial sums [nsplit][16][r]
+  uint32_t kchunk;                  // contraction elements per T split
+  int tunits;                       // > 0: workgroups 0..tunits-1 also compute the T partials
+  uint32_t* flags; uint32_t epoch;  // per T unit: set to epoch once its partials are written
   u16* Y; float* T_save;
 };
 
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void k_tpart(const u16* X, int M, ui
 // Byte offsets of the dynamic LDS regions.  The same function runs on the
 // host (to size the launch) and on the device.
 struct Lds {
-  uint32_t btab, ttab, stab, red, total;
+  uint32_t btab, ttab, tred, stab, red, total;
   uint32_t spitch;                  // floats per row of the scale table
 };
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
@@ -139,7 +144,8 @@ __host__ __device__ inline Lds lds_layout(int tiles, int nbk, int r) {
   L.spitch = ((uint32_t)nbk + 3u) & ~1u;
   L.btab = 0;                                               // B rows of this workgroup, bf16 [rows][r]
   L.ttab = align16(L.btab + rows * (uint32_t)r * 2u);       // T fp32 [16][r]
-  L.stab = align16(L.ttab + 16u * (uint32_t)r * 4u);        // restored block scales fp32 [rows][spitch]
+  L.tred = align16(L.ttab + 16u * (uint32_t)r * 4u);        // a T unit's per-wave sums [8][256]
+  L.stab = L.tred + (uint32_t)WAVES * 256u * 4u;            // restored block scales fp32 [rows][spitch]
   L.red = L.stab;                                           // after the loop: per-wave partial sums
   const uint32_t end_s = L.stab + rows * L.spitch * 4u;
   const uint32_t end_r = L.red + (uint32_t)(WAVES * tiles) * 256u * 4u;
@@ -236,6 +242,40 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   Batch cur, nxt;
   load_batch(cur, p0);
 
+  // ---- a T unit: the partial T of rank tile q over contraction split sp ----
+  if ((int)blockIdx.x < p.tunits) {
+    const int rq = (r + 15) / 16;
+    const int q = (int)blockIdx.x % rq, sp = (int)blockIdx.x / rq;
+    const uint32_t k0 = (uint32_t)sp * p.kchunk, k1 = min(K, k0 + p.kchunk);
+    const auto rA = rsrc(p.A, (uint32_t)r * K * 2u);
+    const uint32_t txrow = (uint32_t)i16 * K * 2u + 16u * (uint32_t)g;
+    const uint32_t tarow = (uint32_t)(16 * q + i16) * K * 2u + 16u * (uint32_t)g;
+    f32x4_t tacc = {0.f, 0.f, 0.f, 0.f};
+    for (uint32_t kk = k0 + 32u * wave; kk < k1; kk += 32u * WAVES * 2) {
+      const uint32_t ka = kk, kb = kk + 32u * WAVES;
+      const bf16x8_t xa = ld16(rX, ka < k1 ? txrow + 2u * ka : OOB), aa = ld16(rA, ka < k1 ? tarow + 2u * ka : OOB);
+      const bf16x8_t xb = ld16(rX, kb < k1 ? txrow + 2u * kb : OOB), ab = ld16(rA, kb < k1 ? tarow + 2u * kb : OOB);
+      tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, aa, tacc, 0, 0, 0);
+      tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ab, tacc, 0, 0, 0);
+    }
+    float* tred = reinterpret_cast<float*>(smem + L.tred);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tred[wave * 256 + (4 * g + e) * 16 + i16] = tacc[e];   // (m, j) of the tile
+    __syncthreads();
+    if (tid < 256) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) v += tred[w * 256 + tid];
+      const int m = tid >> 4, j = 16 * q + (tid & 15);
+      // coherent (device-scope) stores: no cache-wide writeback needed
+      if (j < r) __hip_atomic_store(p.tpart + ((size_t)sp * 16 + m) * r + j, v, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(p.flags + blockIdx.x, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   // ---- tables (their loads queue behind the first batch) ----
   {
     // word e holds the pair (byte & 15, byte >> 4) of byte e / 64: thread tid
@@ -247,27 +287,14 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, __uint_as_float(kNF4LevelBits[i >> 1]));
   }
   float* stab = reinterpret_cast<float*>(smem + L.stab);
-  for (uint32_t e = (uint32_t)tid; e < (uint32_t)ROWS * L.spitch; e += NTHREADS) stab[e] = 0.0f;
+  // the scale table's padding (columns past nbk, rows past this workgroup's
+  // last row) is read by dead pairs and must be finite
+  for (int lr = tid; lr < ROWS; lr += NTHREADS)
+    for (uint32_t b = (uint32_t)nbk; b < L.spitch; ++b) stab[lr * L.spitch + b] = 0.0f;
+  for (uint32_t e = (uint32_t)tid; e < ((uint32_t)ROWS - rows_wg) * L.spitch; e += NTHREADS)
+    stab[rows_wg * L.spitch + e] = 0.0f;
   stage_bytes(smem + L.btab, rB, n0 * (uint32_t)r * 2u, rows_wg * (uint32_t)r * 2u, tid);
   float* ttab = reinterpret_cast<float*>(smem + L.ttab);
-  {
-    // T = the partials summed in split order (all loads of an element in
-    // flight at once; splits past nsplit read as zero); rows m >= M are zero
-    const auto rP = rsrc(p.tpart, (uint32_t)p.nsplit * 16u * (uint32_t)r * 4u);
-    for (int e = tid; e < 16 * r; e += NTHREADS) {
-      float pv[MAX_SPLIT];
-#pragma unroll
-      for (int sp = 0; sp < MAX_SPLIT; ++sp)
-        pv[sp] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rP, 4u * (uint32_t)(sp * 16 * r + e), 0, 0));
-      float v = 0.0f;
-#pragma unroll
-      for (int sp = 0; sp < MAX_SPLIT; ++sp)
-        if (sp < p.nsplit) v += pv[sp];
-      ttab[e] = v;
-      if (blockIdx.x == 0 && e < (int)p.M * r) p.T_save[e] = v;
-    }
-  }
-  __syncthreads();   // the zero fill is done before the scales are written
   {
     // restored scales of this workgroup's blocks [q0, q0 + len): 16 per step
     const uint32_t q0 = n0 * (uint32_t)nbk, len = rows_wg * (uint32_t)nbk;
@@ -384,7 +411,46 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[((wave * TILES + t) * 16 + 4 * g + e) * 16 + i16] = acc[t][e];
+  // T: the partials of workgroups 0..tunits-1 (written early in this kernel;
+  // by now long done -- they wait for nothing before publishing) or of the
+  // separate k_tpart launch.  The wait is bounded: a unit that never reports
+  // poisons this workgroup's output with NaN instead of hanging.
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
   __syncthreads();
+  if (p.tunits > 0) {
+    // coherent loads of the flags (no cache invalidation per poll); the
+    // partials are then read with coherent loads too, issued only after the
+    // barrier that follows every flag being seen
+    for (int u = tid; u < p.tunits; u += NTHREADS) {
+      int spins = 0;
+      while (__hip_atomic_load(p.flags + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+        __builtin_amdgcn_s_sleep(4);
+        if (++spins > (1 << 22)) { s_bad = 1; break; }
+      }
+    }
+    __syncthreads();
+  }
+  {
+    // T = the partials summed in split order (all loads of an element in
+    // flight at once); rows m >= M are zero
+    for (int e = tid; e < 16 * r; e += NTHREADS) {
+      float pv[MAX_SPLIT];
+#pragma unroll
+      for (int sp = 0; sp < MAX_SPLIT; ++sp)
+        pv[sp] = sp < p.nsplit ? __hip_atomic_load(p.tpart + sp * 16 * r + e, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.0f;
+      float v = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < MAX_SPLIT; ++sp)
+        if (sp < p.nsplit) v += pv[sp];
+      ttab[e] = v;
+      if (blockIdx.x == 0 && e < (int)p.M * r) p.T_save[e] = v;
+    }
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0;
   const u16* btab = reinterpret_cast<const u16*>(smem + L.btab);
   constexpr int COLS = 16 * TILES;
   for (int e = tid; e < (int)p.M * COLS; e += NTHREADS) {
@@ -413,7 +479,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       } else {
         for (int j = 0; j < r; ++j) lora += ttab[m * r + j] * bf16_to_f32(btab[c * r + j]);
       }
-      p.Y[(size_t)m * N + n0 + c] = f32_to_bf16(base + p.s * lora);
+      p.Y[(size_t)m * N + n0 + c] = bad ? (u16)0x7FC0u : f32_to_bf16(base + p.s * lora);
     }
   }
 }
@@ -456,6 +522,18 @@ static int pick_tiles(int64_t N, int64_t K, int r) {
   return t;
 }
 
+// Per-call epochs for the T-unit flags: a process-wide counter starting at a
+// random value (so a workspace left over from another process is unlikely to
+// hold a matching flag); 0 is skipped.
+static uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  static std::once_flag once;
+  std::call_once(once, [] { counter.store(std::random_device{}()); });
+  uint32_t e = counter.fetch_add(1) + 1;
+  if (e == 0) e = counter.fetch_add(1) + 1;
+  return e;
+}
+
 // Split of the contraction for the T partials: chunks of at least 512 (a
 // multiple of 64), at most MAX_SPLIT of them.
 struct TSplit {
@@ -473,8 +551,10 @@ static TSplit t_split(int64_t K) {
 
 }  // namespace dec
 
+// workspace: T partials [nsplit][16][r] fp32, then one 32-bit flag per T unit
 int64_t decode_workspace_elems(int64_t K, int r) {
-  return (int64_t)dec::t_split(K).nsplit * 16 * r;
+  const dec::TSplit ts = dec::t_split(K);
+  return (int64_t)ts.nsplit * 16 * r + (int64_t)ts.nsplit * ((r + 15) / 16) + 64;
 }
 
 bool decode_fits(int64_t M, const NF4View& w, int r) {
@@ -488,14 +568,28 @@ bool decode_fits(int64_t M, const NF4View& w, int r) {
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st) {
   const dec::TSplit ts = dec::t_split(w.K);
-  hipLaunchKernelGGL(dec::k_tpart, dim3((unsigned)((r + 15) / 16), (unsigned)ts.nsplit), dim3(64 * dec::TP_WAVES),
-                     0, st, X, (int)M, (uint32_t)w.K, A, r, ts.kchunk, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int tiles = dec::pick_tiles(w.N, w.K, r);
+  const int64_t grid = (w.N + 16 * tiles - 1) / (16 * tiles);
+  const int units = ((r + 15) / 16) * ts.nsplit;
   dec::DecArgs p;
-  p.X = X; p.M = M; p.w = w; p.B = B; p.r = r; p.s = s; p.tpart = ws; p.nsplit = ts.nsplit;
+  p.X = X; p.M = M; p.w = w; p.A = A; p.B = B; p.r = r; p.s = s;
+  p.tpart = ws; p.nsplit = ts.nsplit; p.kchunk = ts.kchunk;
+  p.flags = reinterpret_cast<uint32_t*>(ws + (int64_t)ts.nsplit * 16 * r);
   p.Y = Y; p.T_save = T_save;
-  switch (dec::pick_tiles(w.N, w.K, r)) {
+  if (units <= grid) {
+    // the first workgroups compute the T partials themselves; a fresh epoch
+    // per call tells their flags from those a previous call left behind
+    p.tunits = units;
+    p.epoch = dec::next_epoch();
+  } else {
+    p.tunits = 0;
+    p.epoch = 0;
+    hipLaunchKernelGGL(dec::k_tpart, dim3((unsigned)((r + 15) / 16), (unsigned)ts.nsplit),
+                       dim3(64 * dec::TP_WAVES), 0, st, X, (int)M, (uint32_t)w.K, A, r, ts.kchunk, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (tiles) {
     case 1: return dec::launch_one<1>(p, st);
     case 2: return dec::launch_one<2>(p, st);
     case 3: return dec::launch_one<3>(p, st);

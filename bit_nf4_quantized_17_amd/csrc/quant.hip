@@ -85,6 +85,20 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int64_t b0 = g * 256;
   const int nbg = (int)min<int64_t>(256, nblocks - b0);
 
+  // issue all loads first, then build the bin table while they are in flight
+  f32x4_t v[8][2];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    int bi = p * 32 + wave * 8 + (lane >> 3);
+    if (bi < nbg) {
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(W + (b0 + bi) * 64 + (lane & 7) * 8);
+      v[p][0] = __builtin_nontemporal_load(src);
+      v[p][1] = __builtin_nontemporal_load(src + 1);
+    } else {
+      v[p][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      v[p][1] = v[p][0];
+    }
+  }
   for (int i = tid; i < QBINS; i += 256) {
     float lo = -1.0f + (float)i * (1.0f / 128.0f) - BIN_PAD;
     float hi = -1.0f + (float)(i + 1) * (1.0f / 128.0f) + BIN_PAD;
@@ -99,20 +113,6 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     s_bin[i].base = base;
   }
 
-  // issue all loads first
-  f32x4_t v[8][2];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    int bi = p * 32 + wave * 8 + (lane >> 3);
-    if (bi < nbg) {
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(W + (b0 + bi) * 64 + (lane & 7) * 8);
-      v[p][0] = __builtin_nontemporal_load(src);
-      v[p][1] = __builtin_nontemporal_load(src + 1);
-    } else {
-      v[p][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      v[p][1] = v[p][0];
-    }
-  }
   __syncthreads();  // bin table ready
 
 #pragma unroll
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
       }
     }
     if (bi < nbg) {
-      *reinterpret_cast<uint32_t*>(codes + (b0 + bi) * 32 + (lane & 7) * 4) = word;
+      __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(codes + (b0 + bi) * 32 + (lane & 7) * 4));
       if ((lane & 7) == 0) {
         s_amax[bi] = a;
         if (absmax_out) absmax_out[b0 + bi] = a;
