@@ -88,9 +88,8 @@ int check_layer(const qlora_nf4_weight* w, int64_t M, int r, int compute_dtype) 
 }
 
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  (void)N;
   int64_t elems = skinny_partial_elems(M, K, r);
-  if (M <= 16) elems = std::max(elems, decode_workspace_elems(K, r));
+  if (M <= 16) elems = std::max(elems, decode_workspace_elems(M, N, K, r));
   return align256((size_t)elems * sizeof(float));
 }
 

@@ -84,7 +84,7 @@ hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const f
 // then the weight-streaming kernel; decode_fits says whether a shape can take
 // it and decode_workspace_elems how many fp32 elements of ws it needs.
 bool decode_fits(int64_t M, const NF4View& w, int r);
-int64_t decode_workspace_elems(int64_t K, int r);
+int64_t decode_workspace_elems(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st);
 

@@ -16,16 +16,22 @@
 // kernels multiply the exactly dequantized bf16 weight instead; both round
 // the weight's relative value once to bf16 precision.)
 //
-// Two kernels per call.  k_tpart computes T = X A^T as fixed split-K partial
-// sums (a few dozen workgroups; A is read once).  k_decode streams the
-// weight: one workgroup of 8 waves per 16*TILES output columns (W rows),
-// sized so that the grid is about one workgroup per compute unit; each wave
-// takes an eighth of the contraction (rotated by the workgroup index, so that
-// the workgroups do not all stream the same column range of the weight at
-// once) for all its tiles, so each X fragment it loads serves TILES weight
-// tiles.  Codes are read straight from HBM into registers, 16 bytes a lane:
-// lane (i, g) of a 16-row tile loads bytes 16g..16g+15 of a pair of blocks of
-// row i, so the lower half-wave holds the first block and the upper half the
+// k_decode streams the weight: one workgroup of 8 waves per 16*TILES output
+// columns (W rows) and per part of the contraction, the grid sized to about
+// one workgroup per compute unit.  Each wave takes an eighth of its part
+// (rotated by the workgroup index, so that the workgroups do not all stream
+// the same column range of the weight at once) for all its tiles, so each X
+// fragment it loads serves TILES weight tiles.  Cutting the contraction into
+// parts lets a workgroup cover more columns when the layer has few: the
+// parts other than the last store their fp32 sums in the workspace, and the
+// last part of each column group adds them, in part order, to its own.  T =
+// X A^T is computed as fixed split-K partial sums by the first workgroups of
+// the same launch (or, when there are more of them than workgroups, by a
+// separate k_tpart launch first; A is read once).
+//
+// Codes are read straight from HBM into registers, 16 bytes a lane: lane
+// (i, g) of a 16-row tile loads bytes 16g..16g+15 of a pair of blocks of row
+// i, so the lower half-wave holds the first block and the upper half the
 // second; two v_permlane32_swap exchanges then leave every lane with 16 codes
 // of each block, at contraction offset 32(g&1) + 16(g>>1) inside the block,
 // and X is loaded with the same permutation, which leaves each block's sum
@@ -34,11 +40,15 @@
 // (about 16 bytes a clock, shared by the code and X loads) works through them
 // while the wave computes instead of stalling its issue.
 //
-// The restored scales of all the workgroup's blocks, the LoRA factor B of its
-// columns and T (summed from the partials in a fixed order; workgroup 0 also
-// writes it to T_save) are put in LDS at the start, behind the first batch's
-// loads.  The eight partial results are summed in LDS in wave order, so
-// results do not depend on timing.
+// The restored scales of the workgroup's blocks and the LoRA factor B of its
+// columns are put in LDS at the start, behind the first batch's loads; T
+// (summed from the partials in a fixed order; the first column group also
+// writes it to T_save) at the end.  The eight waves' results are summed in
+// LDS in wave order, so results do not depend on timing.  Producers (T
+// units, parts other than the last) publish each sum as one coherent 64-bit
+// word tagged with a per-call epoch, which the consumer polls directly; they
+// have lower workgroup indices than every consumer and never wait, so the
+// waits always end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -61,6 +71,7 @@ constexpr int MAX_TILES = 8;
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every range this path uses
 constexpr int TP_WAVES = 4;             // waves of a k_tpart workgroup
 constexpr int MAX_SPLIT = 16;           // T partials a decode workgroup sums
+constexpr int MAX_KPARTS = 4;           // contraction parts of the weight stream
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
@@ -69,10 +80,15 @@ struct DecArgs {
   const u16* X; int64_t M;          // X [M][K], M <= 16
   NF4View w;                        // W [N][K]
   const u16* A; const u16* B; int r; float s;
-  float* tpart; int nsplit;         // T partial sums [nsplit][16][r]
+  // Partial sums handed between workgroups are tagged words: epoch << 32 |
+  // fp32 bits, written and read with coherent 64-bit accesses, so a consumer
+  // sees a value and its readiness in one load and no fence is needed.
+  uint64_t* tpart; int nsplit;      // T partial sums [nsplit][16][r]
   uint32_t kchunk;                  // contraction elements per T split
   int tunits;                       // > 0: workgroups 0..tunits-1 also compute the T partials
-  uint32_t* flags; uint32_t epoch;  // per T unit: set to epoch once its partials are written
+  uint32_t epoch;                   // this call's tag (never 0)
+  int kparts, gcols;                // contraction parts x column groups = the grid
+  uint64_t* ypart;                  // parts 0..kparts-2: partial Y [part][M][N]
   u16* Y; float* T_save;
 };
 
@@ -84,6 +100,47 @@ __device__ __forceinline__ bf16x8_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// s_waitcnt for the vector-memory counter only: at most n loads outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+__device__ __forceinline__ void put_tagged(uint64_t* dst, float v, uint32_t epoch) {
+  __hip_atomic_store(dst, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_tagged(const uint64_t* src) {
+  return __hip_atomic_load(const_cast<uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A first read that may be served by this die's cache: words that many
+// workgroups read (the T partials) then come from memory about once per
+// cache.  A stale copy carries an older tag, and the retries of await_tagged
+// read coherently.
+__device__ __forceinline__ uint64_t get_tagged_cached(const uint64_t* src) {
+  return __hip_atomic_load(const_cast<uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Wait until every word of w[0..n) carries `epoch`, re-reading the others
+// after a short sleep; gives up (returns false) after about 0.4 s, so that a
+// producer that never writes cannot hang the caller.
+template <int CAP>
+__device__ __forceinline__ bool await_tagged(uint64_t (&w)[CAP], const uint64_t* const (&src)[CAP], int n,
+                                             uint32_t epoch) {
+  for (int spins = 0;; ++spins) {
+    bool ready = true;
+#pragma unroll
+    for (int i = 0; i < CAP; ++i)
+      if (i < n && (uint32_t)(w[i] >> 32) != epoch) ready = false;
+    if (ready) return true;
+    if (spins > (1 << 20)) return false;
+    __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+    for (int i = 0; i < CAP; ++i)
+      if (i < n && (uint32_t)(w[i] >> 32) != epoch) w[i] = get_tagged(src[i]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // T partials: workgroup (q, s) sums X[m][k] A[16q + j][k] over k in split s
 // (kchunk elements, a multiple of 64) into part[s][m][16q + j]; rows m >= M
@@ -91,7 +148,7 @@ __device__ __forceinline__ bf16x8_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // contraction steps in turn and are summed in LDS in wave order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * TP_WAVES) void k_tpart(const u16* X, int M, uint32_t K, const u16* A, int r,
-                                                         uint32_t kchunk, float* part) {
+                                                         uint32_t kchunk, uint64_t* part, uint32_t epoch) {
   __shared__ float red[TP_WAVES][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, i16 = lane & 15, g = lane >> 4;
   const int q = blockIdx.x;
@@ -122,7 +179,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void k_tpart(const u16* X, int M, ui
 #pragma unroll
     for (int w = 0; w < TP_WAVES; ++w) v += red[w][e];
     const int m = e >> 4, j = 16 * q + (e & 15);
-    if (j < r) part[((size_t)blockIdx.y * 16 + m) * r + j] = v;
+    if (j < r) put_tagged(part + ((size_t)blockIdx.y * 16 + m) * r + j, v, epoch);
   }
 }
 
@@ -130,53 +187,53 @@ __global__ __launch_bounds__(64 * TP_WAVES) void k_tpart(const u16* X, int M, ui
 // the weight stream
 // ---------------------------------------------------------------------------
 // Byte offsets of the dynamic LDS regions.  The same function runs on the
-// host (to size the launch) and on the device.
+// host (to size the launch) and on the device.  Regions that receive
+// direct-to-LDS loads are rounded up to what one wave's load instruction
+// writes (1 KB, or 256 bytes for 4-byte loads), so that the zeros written by
+// out-of-range lanes stay inside them.
 struct Lds {
-  uint32_t btab, ttab, tred, stab, red, total;
+  uint32_t btab, ttab, tred, stab, tstage, qstage, dstage, tails, red, total;
   uint32_t spitch;                  // floats per row of the scale table
+  bool qalias;                      // the staged scale bytes lie inside the scale table
 };
-__host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
-__host__ __device__ inline Lds lds_layout(int tiles, int nbk, int r) {
+__host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1u) / a * a; }
+// nbk: 64-blocks per row of W; nbkp: the blocks of a row this workgroup covers
+__host__ __device__ inline Lds lds_layout(int tiles, int nbk, int nbkp, int r) {
   Lds L;
   const uint32_t rows = 16u * (uint32_t)tiles;
-  // an even pitch of nbk + 2 or more keeps 8-byte reads aligned and puts the
+  // an even pitch of nbkp + 2 or more keeps 8-byte reads aligned and puts the
   // 16 rows a wave reads at once in different banks
-  L.spitch = ((uint32_t)nbk + 3u) & ~1u;
-  L.btab = 0;                                               // B rows of this workgroup, bf16 [rows][r]
-  L.ttab = align16(L.btab + rows * (uint32_t)r * 2u);       // T fp32 [16][r]
-  L.tred = align16(L.ttab + 16u * (uint32_t)r * 4u);        // a T unit's per-wave sums [8][256]
-  L.stab = L.tred + (uint32_t)WAVES * 256u * 4u;            // restored block scales fp32 [rows][spitch]
-  L.red = L.stab;                                           // after the loop: per-wave partial sums
-  const uint32_t end_s = L.stab + rows * L.spitch * 4u;
-  const uint32_t end_r = L.red + (uint32_t)(WAVES * tiles) * 256u * 4u;
+  L.spitch = ((uint32_t)nbkp + 3u) & ~1u;
+  L.btab = 0;                                                    // B rows, bf16 [rows][r]
+  L.ttab = align_up(L.btab + rows * (uint32_t)r * 2u, 1024u);    // T fp32 [16][r]
+  L.tred = align_up(L.ttab + 16u * (uint32_t)r * 4u, 16u);       // a T unit's per-wave sums [8][256]
+  // overlay: restored block scales fp32 [rows][spitch]; before them a T
+  // unit's staged operands [8 waves][4][1 KB] at its start and the raw scale
+  // bytes (16 per chunk) at its end, when all of those fit in two chunks a
+  // thread (the fill reads them all before writing); after the loop the
+  // per-wave partial sums [8][tiles][1 KB]
+  L.stab = L.tred + (uint32_t)WAVES * 256u * 4u;
+  L.tstage = L.stab;
+  L.red = L.stab;
+  const uint32_t sbytes = rows * L.spitch * 4u, tbytes = (uint32_t)WAVES * 4096u;
+  const uint32_t nch = (rows * (uint32_t)nbkp + 15u) / 16u;
+  const uint32_t qsz = align_up(16u * nch, 1024u);
+  L.qalias = nch <= 2u * NTHREADS;
+  if (L.qalias) {
+    const uint32_t ov = align_up(sbytes > tbytes + qsz ? sbytes : tbytes + qsz, 16u);
+    L.qstage = L.stab + ov - qsz;
+    L.dstage = L.stab + ov;
+  } else {
+    const uint32_t ov = align_up(sbytes > tbytes ? sbytes : tbytes, 16u);
+    L.qstage = L.stab + ov;
+    L.dstage = L.qstage + qsz;
+  }
+  const uint32_t ngr = ((rows - 1u) * (uint32_t)nbk + (uint32_t)nbkp + 255u) / 256u + 2u;
+  L.tails = L.dstage + align_up(4u * ngr, 256u);                 // 2 x 64 dwords: end-of-array bytes
+  const uint32_t end_s = L.tails + 512u;
+  const uint32_t end_r = L.red + (uint32_t)(WAVES * tiles) * 1024u;
   L.total = end_s > end_r ? end_s : end_r;
   return L;
-}
-
-// Copy `len` bytes from buffer offset `goff` (16-byte aligned) to LDS `dst`
-// (16-byte aligned): 16-byte loads, up to four per thread in flight before
-// the stores, then single bytes for a tail under 16.
-__device__ __forceinline__ void stage_bytes(uint8_t* dst, __amdgpu_buffer_rsrc_t src, uint32_t goff,
-                                            uint32_t len, int tid) {
-  const uint32_t nchunk = len >> 4;
-  for (uint32_t base = (uint32_t)tid; base < nchunk; base += 4 * NTHREADS) {
-    u32x4v v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t i = base + (uint32_t)(u * NTHREADS);
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(src, i < nchunk ? goff + 16u * i : OOB, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t i = base + (uint32_t)(u * NTHREADS);
-      if (i < nchunk) *reinterpret_cast<u32x4v*>(dst + 16u * i) = v[u];
-    }
-  }
-  const uint32_t tail = len & 15u;
-  if ((uint32_t)tid < tail) {
-    const uint32_t i = (nchunk << 4) + (uint32_t)tid;
-    dst[i] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(src, goff + i, 0, 0);
-  }
 }
 
 // TILES: 16-column tiles per workgroup.  One batch = NP pairs of blocks.
@@ -192,10 +249,16 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   const uint32_t K = (uint32_t)p.w.K, RB = K / 2u;   // code bytes per row
   const int nbk = (int)(K / 64), npair = (nbk + 1) / 2;
   const uint32_t N = (uint32_t)p.w.N;
-  const uint32_t n0 = blockIdx.x * (uint32_t)ROWS;
+  // column group and contraction part; parts other than the last hand their
+  // fp32 partial sums to the last, which finishes the output
+  const int kp = (int)blockIdx.x / p.gcols;
+  const uint32_t n0 = (uint32_t)((int)blockIdx.x % p.gcols) * (uint32_t)ROWS;
   const uint32_t rows_wg = min((uint32_t)ROWS, N - n0);
+  const bool last = kp == p.kparts - 1;
+  const int wp0 = kp * npair / p.kparts, wp1 = (kp + 1) * npair / p.kparts;   // this part's pairs
+  const int kb0 = 2 * wp0, nbkp = min(nbk, 2 * wp1) - kb0;                    // and blocks
   const int r = p.r;
-  const Lds L = lds_layout(TILES, nbk, r);
+  const Lds L = lds_layout(TILES, nbk, nbkp, r);
 
   const auto rX = rsrc(p.X, (uint32_t)p.M * K * 2u);
   const auto rC = rsrc(p.w.codes, N * RB);
@@ -204,9 +267,12 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   const auto rD = rsrc(p.w.dscale, 4u * ((nb_all + 255u) / 256u));
   const auto rB = rsrc(p.B, N * (uint32_t)r * 2u);
 
-  // this wave's pairs of blocks, and the per-lane load offsets
-  const int wv = (wave + (int)blockIdx.x) & (WAVES - 1);
-  const int p0 = wv * npair / WAVES, p1 = (wv + 1) * npair / WAVES;
+  // this wave's pairs of blocks (computed from the wave index as a scalar,
+  // so that the compiler sees them uniform and selects load addresses
+  // without branching), and the per-lane load offsets
+  const int wsc = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = (wsc + (int)blockIdx.x) & (WAVES - 1);
+  const int p0 = wp0 + wv * (wp1 - wp0) / WAVES, p1 = wp0 + (wv + 1) * (wp1 - wp0) / WAVES;
   uint32_t crow[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) crow[t] = (n0 + 16u * t + (uint32_t)i16) * RB + 16u * (uint32_t)g;
@@ -226,7 +292,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kb = 2 * pr + h;
-        const uint32_t xo = live && kb < nbk ? xrow + 128u * (uint32_t)kb : OOB;
+        const uint32_t xo = (live & (kb < nbk)) ? xrow + 128u * (uint32_t)kb : OOB;   // no short circuit: no branch
         bt.x[u][h][0] = ld16(rX, xo);     // rows >= M are past the buffer: zero
         bt.x[u][h][1] = ld16(rX, xo + 16u);
       }
@@ -239,24 +305,134 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       for (int t = 0; t < TILES; ++t) load_slot(bt, pr0, u, t);
   };
 
-  Batch cur, nxt;
-  load_batch(cur, p0);
+  typedef __attribute__((address_space(3))) void* lds_ptr;
 
-  // ---- a T unit: the partial T of rank tile q over contraction split sp ----
-  if ((int)blockIdx.x < p.tunits) {
-    const int rq = (r + 15) / 16;
-    const int q = (int)blockIdx.x % rq, sp = (int)blockIdx.x / rq;
-    const uint32_t k0 = (uint32_t)sp * p.kchunk, k1 = min(K, k0 + p.kchunk);
-    const auto rA = rsrc(p.A, (uint32_t)r * K * 2u);
-    const uint32_t txrow = (uint32_t)i16 * K * 2u + 16u * (uint32_t)g;
-    const uint32_t tarow = (uint32_t)(16 * q + i16) * K * 2u + 16u * (uint32_t)g;
+  // ---- tables that need no loads ----
+  {
+    // word e holds the pair (byte & 15, byte >> 4) of byte e / 64: thread tid
+    // writes bytes tid/64 + 8i, whose low nibble is tid/64 or tid/64 + 8
+    const float lo0 = __uint_as_float(kNF4LevelBits[wsc]);
+    const float lo1 = __uint_as_float(kNF4LevelBits[wsc + 8]);
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, __uint_as_float(kNF4LevelBits[i >> 1]));
+  }
+  float* stab = reinterpret_cast<float*>(smem + L.stab);
+  float* ttab = reinterpret_cast<float*>(smem + L.ttab);
+
+  // ---- set-up loads, issued before the first batch and written straight
+  //      to LDS: loads complete in order, so that waiting for these does not
+  //      wait for the batch, and no register is tied up by them ----
+  // (a) a T unit's first two contraction steps: the partial T of rank tile tq
+  //     over contraction split tsp; lane (i16, g) stages 16 bytes of X row i16
+  //     and of A row 16 tq + i16, as its MFMA operands
+  const bool tunit = (int)blockIdx.x < p.tunits;
+  const int rq = (r + 15) / 16;
+  const int tq = (int)blockIdx.x % rq, tsp = (int)blockIdx.x / rq;
+  const uint32_t tk0 = (uint32_t)tsp * p.kchunk, tk1 = min(K, tk0 + p.kchunk);
+  const auto rA = rsrc(p.A, (uint32_t)r * K * 2u);
+  const uint32_t txrow = (uint32_t)i16 * K * 2u + 16u * (uint32_t)g;
+  const uint32_t tarow = (uint32_t)(16 * tq + i16) * K * 2u + 16u * (uint32_t)g;
+  uint8_t* tst = smem + L.tstage + 4096u * (uint32_t)wsc;   // [X0, A0, X1, A1] x 1 KB
+  if (tunit) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t k = tk0 + 32u * (uint32_t)(wsc + WAVES * h);
+      if (k < tk1) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr)(tst + 2048u * h), 16, txrow + 2u * k, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(tst + 2048u * h + 1024u), 16, tarow + 2u * k, 0, 0, 0);
+      }
+    }
+  }
+  // (b) the LoRA factor B of this workgroup's columns (the last part only), in
+  //     16-byte chunks that lie wholly inside B; the few elements after the
+  //     last such chunk (at the end of B only) come as one 2-byte load a lane,
+  //     which the hardware writes as a dword to the tails area
+  const uint32_t bsize = N * (uint32_t)r * 2u;
+  const uint32_t bgoff = n0 * (uint32_t)r * 2u, blen = last ? rows_wg * (uint32_t)r * 2u : 0u;
+  const uint32_t bnch = min((blen + 15u) / 16u, (bsize - bgoff) / 16u);
+  for (uint32_t u = (uint32_t)wsc; 64u * u < bnch; u += WAVES) {
+    const uint32_t i = 64u * u + (uint32_t)lane;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(smem + L.btab + 1024u * u), 16,
+                                             i < bnch ? bgoff + 16u * i : OOB, 0, 0, 0);
+  }
+  const uint32_t btail = blen > 16u * bnch ? (blen - 16u * bnch) / 2u : 0u;   // bf16 elements, < 8
+  if (wsc == 0 && btail > 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(smem + L.tails), 2,
+                                             (uint32_t)lane < btail ? bgoff + 16u * bnch + 2u * (uint32_t)lane : OOB,
+                                             0, 0, 0);
+  // (c) the raw 8-bit scales of this workgroup's blocks, 16 per chunk: with
+  //     one part the blocks [q0, q0 + rows_wg * nbk) are contiguous; with more,
+  //     each row holds a segment of nbkp blocks (a multiple of 16, 16-byte
+  //     aligned).  Chunk c is staged at qstage + 16 c, so staged byte f is
+  //     block (f / nbkp, f % nbkp) of the workgroup's rows in both cases.
+  //     Chunks wholly inside the qscale array come straight to LDS; the bytes
+  //     of a last, partial one (at the end of the array only) come as one
+  //     byte load a lane, written as a dword to the tails area.
+  const bool flat = p.kparts == 1;
+  const uint32_t q0 = n0 * (uint32_t)nbk, qlen = rows_wg * (uint32_t)nbkp;
+  const uint32_t cpr = (uint32_t)nbkp / 16u;   // chunks per row segment (parts > 1)
+  const uint32_t nch = (qlen + 15u) / 16u;
+  auto chunk_at = [&](uint32_t c, uint32_t& lr, uint32_t& b, uint32_t& qoff) {
+    if (flat) { const uint32_t f0 = 16u * c; lr = f0 / (uint32_t)nbk; b = f0 - lr * (uint32_t)nbk; qoff = q0 + f0; }
+    else { lr = c / cpr; b = 16u * (c - lr * cpr); qoff = (n0 + lr) * (uint32_t)nbk + (uint32_t)kb0 + b; }
+  };
+  const uint32_t nch_dma = flat ? min(nch, (nb_all - q0) / 16u) : nch;
+  for (uint32_t u = (uint32_t)wsc; 64u * u < nch_dma; u += WAVES) {
+    const uint32_t c = 64u * u + (uint32_t)lane;
+    uint32_t lr, b, qoff;
+    chunk_at(c, lr, b, qoff);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr)(smem + L.qstage + 1024u * u), 16, c < nch_dma ? qoff : OOB,
+                                             0, 0, 0);
+  }
+  const uint32_t qtail = qlen - min(qlen, 16u * nch_dma);   // < 16 bytes
+  if (wsc == 0 && qtail > 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr)(smem + L.tails + 256u), 1,
+                                             (uint32_t)lane < qtail ? q0 + 16u * nch_dma + (uint32_t)lane : OOB,
+                                             0, 0, 0);
+  // (d) the fp32 second-level constants of every group those blocks touch
+  const uint32_t gfirst = (flat ? q0 : q0 + (uint32_t)kb0) >> 8;
+  const uint32_t glast = (flat ? q0 + qlen - 1u : (n0 + rows_wg - 1u) * (uint32_t)nbk + (uint32_t)kb0 + (uint32_t)nbkp - 1u) >> 8;
+  const uint32_t ngr = glast - gfirst + 1u;
+  for (uint32_t u = (uint32_t)wsc; 64u * u < ngr; u += WAVES) {
+    const uint32_t gi = 64u * u + (uint32_t)lane;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_ptr)(smem + L.dstage + 256u * u), 4,
+                                             gi < ngr ? 4u * (gfirst + gi) : OOB, 0, 0, 0);
+  }
+
+  // the first two batches go out now, so that the memory system has work
+  // while the tables are built
+  Batch cur, nxt;
+  __builtin_amdgcn_sched_barrier(0);   // keep every set-up load ahead of the batches
+  load_batch(cur, p0);
+  load_batch(nxt, p0 + NP);
+  __builtin_amdgcn_sched_barrier(0);
+  // the set-up loads are complete once no more than the two batches' loads
+  // are outstanding
+  wait_vm<2 * NP * (TILES + 4)>();
+
+  // ---- a T unit: finish its partial T ----
+  if (tunit) {
     f32x4_t tacc = {0.f, 0.f, 0.f, 0.f};
-    for (uint32_t kk = k0 + 32u * wave; kk < k1; kk += 32u * WAVES * 2) {
-      const uint32_t ka = kk, kb = kk + 32u * WAVES;
-      const bf16x8_t xa = ld16(rX, ka < k1 ? txrow + 2u * ka : OOB), aa = ld16(rA, ka < k1 ? tarow + 2u * ka : OOB);
-      const bf16x8_t xb = ld16(rX, kb < k1 ? txrow + 2u * kb : OOB), ab = ld16(rA, kb < k1 ? tarow + 2u * kb : OOB);
-      tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, aa, tacc, 0, 0, 0);
-      tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ab, tacc, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t k = tk0 + 32u * (uint32_t)(wsc + WAVES * h);
+      if (k < tk1) {
+        const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(tst + 2048u * h + 16u * (uint32_t)lane);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(tst + 2048u * h + 1024u + 16u * (uint32_t)lane);
+        tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, av, tacc, 0, 0, 0);
+      }
+    }
+    // further steps (a split longer than 16 steps) load behind the batch
+    if (tk1 - tk0 > 64u * WAVES) {
+      for (uint32_t kk = tk0 + 32u * (uint32_t)(wave + 2 * WAVES); kk < tk1; kk += 32u * WAVES * 2) {
+        const uint32_t ka = kk, kb = kk + 32u * WAVES;
+        const bf16x8_t xa = ld16(rX, ka < tk1 ? txrow + 2u * ka : OOB), aa = ld16(rA, ka < tk1 ? tarow + 2u * ka : OOB);
+        const bf16x8_t xb = ld16(rX, kb < tk1 ? txrow + 2u * kb : OOB), ab = ld16(rA, kb < tk1 ? tarow + 2u * kb : OOB);
+        tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, aa, tacc, 0, 0, 0);
+        tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ab, tacc, 0, 0, 0);
+      }
+      wait_vm<0>();
     }
     float* tred = reinterpret_cast<float*>(smem + L.tred);
 #pragma unroll
@@ -266,75 +442,77 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) v += tred[w * 256 + tid];
-      const int m = tid >> 4, j = 16 * q + (tid & 15);
-      // coherent (device-scope) stores: no cache-wide writeback needed
-      if (j < r) __hip_atomic_store(p.tpart + ((size_t)sp * 16 + m) * r + j, v, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+      const int m = tid >> 4, j = 16 * tq + (tid & 15);
+      if (j < r) put_tagged(p.tpart + ((size_t)tsp * 16 + m) * r + j, v, p.epoch);
     }
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(p.flags + blockIdx.x, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // wave 0 moves the end-of-array elements it staged into place; then every
+  // wave's staged data is in LDS (and a T unit is done with its staging
+  // area, which the scale table overwrites)
+  {
+    const uint32_t* tl = reinterpret_cast<const uint32_t*>(smem + L.tails);
+    if ((uint32_t)tid < btail) reinterpret_cast<uint16_t*>(smem + L.btab)[8u * bnch + (uint32_t)tid] = (uint16_t)tl[tid];
+    if ((uint32_t)tid < qtail) (smem + L.qstage)[16u * nch_dma + (uint32_t)tid] = (uint8_t)tl[64 + tid];
+  }
+  __syncthreads();
 
-  // ---- tables (their loads queue behind the first batch) ----
+  // ---- the restored scales s_b = fl32(E4M3(q_b) * d_g), from the staged bytes ----
   {
-    // word e holds the pair (byte & 15, byte >> 4) of byte e / 64: thread tid
-    // writes bytes tid/64 + 8i, whose low nibble is tid/64 or tid/64 + 8
-    const float lo0 = __uint_as_float(kNF4LevelBits[tid >> 6]);
-    const float lo1 = __uint_as_float(kNF4LevelBits[(tid >> 6) + 8]);
+    // A chunk is 16 blocks at a 16-aligned position of the qscale array, so
+    // it lies in one group of 256 (one d_g); when nbkp is a multiple of 16 it
+    // also lies in one row.  E4M3 is decoded by the hardware conversion (OCP
+    // E4M3FN on this target, exact).
+    const float* dst = reinterpret_cast<const float*>(smem + L.dstage);
+    const bool in_row = (nbkp & 15) == 0;
+    auto fill_chunk = [&](uint32_t c, const u32x4v& v) {
+      uint32_t lr, b, qoff;
+      chunk_at(c, lr, b, qoff);
+      const float d = dst[(qoff >> 8) - gfirst];
+      float f[16];
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, __uint_as_float(kNF4LevelBits[i >> 1]));
-  }
-  float* stab = reinterpret_cast<float*>(smem + L.stab);
-  // the scale table's padding (columns past nbk, rows past this workgroup's
-  // last row) is read by dead pairs and must be finite
-  for (int lr = tid; lr < ROWS; lr += NTHREADS)
-    for (uint32_t b = (uint32_t)nbk; b < L.spitch; ++b) stab[lr * L.spitch + b] = 0.0f;
-  for (uint32_t e = (uint32_t)tid; e < ((uint32_t)ROWS - rows_wg) * L.spitch; e += NTHREADS)
-    stab[rows_wg * L.spitch + e] = 0.0f;
-  stage_bytes(smem + L.btab, rB, n0 * (uint32_t)r * 2u, rows_wg * (uint32_t)r * 2u, tid);
-  float* ttab = reinterpret_cast<float*>(smem + L.ttab);
-  {
-    // restored scales of this workgroup's blocks [q0, q0 + len): 16 per step
-    const uint32_t q0 = n0 * (uint32_t)nbk, len = rows_wg * (uint32_t)nbk;
-    auto fill = [&](uint32_t c, const u32x4v& v, float da, float db, uint32_t ga) {
-      const uint32_t f0 = 16u * c;
-      uint32_t lr = f0 / (uint32_t)nbk, b = f0 - lr * (uint32_t)nbk;
+      for (int w = 0; w < 4; ++w) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
+        f[4 * w] = lo[0] * d;
+        f[4 * w + 1] = lo[1] * d;
+        f[4 * w + 2] = hi[0] * d;
+        f[4 * w + 3] = hi[1] * d;
+      }
+      if (in_row) {
+        float* row = stab + lr * L.spitch + b;   // 8-byte aligned: even pitch, b a multiple of 16
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (f0 + k < len) {
-          const float d = ((q0 + f0 + k) >> 8) == ga ? da : db;
-          stab[lr * L.spitch + b] = e4m3_decode((v[k >> 2] >> (8 * (k & 3))) & 127u) * d;
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x2v*>(row + 2 * j) = f32x2v{f[2 * j], f[2 * j + 1]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (16u * c + k < qlen) stab[lr * L.spitch + b] = f[k];
+          if (++b == (uint32_t)nbkp) { b = 0; ++lr; }
         }
-        if (++b == (uint32_t)nbk) { b = 0; ++lr; }
       }
     };
-    // 16 scale bytes per chunk; a chunk that runs past the workgroup's blocks
-    // is read byte by byte (the qscale array may end there)
-    auto load_q = [&](uint32_t c) -> u32x4v {
-      const uint32_t f0 = 16u * c;
-      if (f0 + 16u <= len) return __builtin_amdgcn_raw_buffer_load_b128(rQ, q0 + f0, 0, 0);
-      u32x4v v = {0u, 0u, 0u, 0u};
-      for (uint32_t k = 0; f0 + k < len; ++k)
-        v[k >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rQ, q0 + f0 + k, 0, 0) << (8 * (k & 3));
-      return v;
+    // the scale table's padding (columns past nbkp, rows past this
+    // workgroup's last row) is read by dead pairs and must be finite
+    auto zero_padding = [&]() {
+      for (int lr = tid; lr < ROWS; lr += NTHREADS)
+        for (uint32_t b = (uint32_t)nbkp; b < L.spitch; ++b) stab[lr * L.spitch + b] = 0.0f;
+      for (uint32_t e = (uint32_t)tid; e < ((uint32_t)ROWS - rows_wg) * L.spitch; e += NTHREADS)
+        stab[rows_wg * L.spitch + e] = 0.0f;
     };
-    auto load_d = [&](uint32_t gi) -> float {
-      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, 4u * gi, 0, 0));
-    };
-    const uint32_t nch = (len + 15u) / 16u;
-    for (uint32_t c0 = (uint32_t)tid; c0 < nch; c0 += 2 * NTHREADS) {
-      const uint32_t c1 = c0 + NTHREADS;
-      const bool two = c1 < nch;
-      const u32x4v v0 = load_q(c0);
-      const u32x4v v1 = two ? load_q(c1) : u32x4v{0u, 0u, 0u, 0u};
-      const uint32_t ga0 = (q0 + 16u * c0) >> 8, gb0 = (q0 + min(16u * c0 + 15u, len - 1u)) >> 8;
-      const uint32_t ga1 = (q0 + 16u * c1) >> 8, gb1 = (q0 + min(16u * c1 + 15u, len - 1u)) >> 8;
-      const float da0 = load_d(ga0), db0 = load_d(gb0);
-      const float da1 = load_d(two ? ga1 : ga0), db1 = load_d(two ? gb1 : gb0);
-      fill(c0, v0, da0, db0, ga0);
-      if (two) fill(c1, v1, da1, db1, ga1);
+    const uint8_t* qst = smem + L.qstage;
+    if (L.qalias) {
+      // the staged bytes share the table's space: read them all first
+      const uint32_t c0 = (uint32_t)tid, c1 = c0 + NTHREADS;
+      u32x4v v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+      if (c0 < nch) v0 = *reinterpret_cast<const u32x4v*>(qst + 16u * c0);
+      if (c1 < nch) v1 = *reinterpret_cast<const u32x4v*>(qst + 16u * c1);
+      __syncthreads();
+      zero_padding();
+      if (c0 < nch) fill_chunk(c0, v0);
+      if (c1 < nch) fill_chunk(c1, v1);
+    } else {
+      zero_padding();
+      for (uint32_t c = (uint32_t)tid; c < nch; c += NTHREADS)
+        fill_chunk(c, *reinterpret_cast<const u32x4v*>(qst + 16u * c));
     }
   }
   __syncthreads();
@@ -359,7 +537,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     for (int u = 0; u < NP; ++u) {
       // a pair past the row's end (the last batch of a wave may hold one) has
       // zero X; any finite scale then adds nothing
-      const int prs = min(pr0 + u, npair - 1);
+      const int prs = min(pr0 + u, wp1 - 1);
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         if constexpr (decltype(prefetch)::value) load_slot(nb, pr0 + NP, u, t);
@@ -368,7 +546,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
         const auto s02 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].x, bt.c[u][t].z, false, false);
         const auto s13 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].y, bt.c[u][t].w, false, false);
         const uint32_t w[4] = {s02[0], s13[0], s02[1], s13[1]};
-        const f32x2v sc = *reinterpret_cast<const f32x2v*>(stab + (16 * t + i16) * L.spitch + 2 * prs);
+        const f32x2v sc = *reinterpret_cast<const f32x2v*>(stab + (16 * t + i16) * L.spitch + 2 * (prs - wp0));
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4v wa = {lookup(w[2 * h], 0), lookup(w[2 * h], 1), lookup(w[2 * h], 2), lookup(w[2 * h], 3)};
@@ -387,20 +565,25 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   };
 
   // two batches ping-pong (no register copies, which would wait for the
-  // loads); the tail issues no loads past this wave's last pair, since even a
-  // load that returns zero costs address-unit time
+  // loads): both are in flight at the first step, which therefore loads
+  // nothing; the tail issues no loads past this wave's last pair, since even
+  // a load that returns zero costs address-unit time
   const std::integral_constant<bool, true> pf;
   const std::integral_constant<bool, false> nopf;
   int pr = p0;
-  for (; pr + 2 * NP < p1; pr += 2 * NP) {
-    step(cur, nxt, pr, pf);
-    step(nxt, cur, pr + NP, pf);
-  }
-  if (pr + NP < p1) {
-    step(cur, nxt, pr, pf);
-    step(nxt, cur, pr + NP, nopf);
-  } else if (pr < p1) {
+  if (pr < p1) {
     step(cur, nxt, pr, nopf);
+    pr += NP;
+    for (; pr + 2 * NP < p1; pr += 2 * NP) {
+      step(nxt, cur, pr, pf);
+      step(cur, nxt, pr + NP, pf);
+    }
+    if (pr + NP < p1) {
+      step(nxt, cur, pr, pf);
+      step(cur, nxt, pr + NP, nopf);
+    } else if (pr < p1) {
+      step(nxt, cur, pr, nopf);
+    }
   }
 
   // ---- cross-wave sums (fixed wave order), LoRA term, store ----
@@ -411,52 +594,79 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[((wave * TILES + t) * 16 + 4 * g + e) * 16 + i16] = acc[t][e];
-  // T: the partials of workgroups 0..tunits-1 (written early in this kernel;
-  // by now long done -- they wait for nothing before publishing) or of the
-  // separate k_tpart launch.  The wait is bounded: a unit that never reports
-  // poisons this workgroup's output with NaN instead of hanging.
   __shared__ int s_bad;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  if (p.tunits > 0) {
-    // coherent loads of the flags (no cache invalidation per poll); the
-    // partials are then read with coherent loads too, issued only after the
-    // barrier that follows every flag being seen
-    for (int u = tid; u < p.tunits; u += NTHREADS) {
-      int spins = 0;
-      while (__hip_atomic_load(p.flags + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-        __builtin_amdgcn_s_sleep(4);
-        if (++spins > (1 << 22)) { s_bad = 1; break; }
+  constexpr int COLS = 16 * TILES;
+  const int cg = (int)blockIdx.x % p.gcols;
+  if (!last) {
+    // a part that is not the last: its sums (fixed wave order) go to the
+    // workspace with coherent stores, then its flag is raised
+    uint64_t* yp = p.ypart + (size_t)kp * (size_t)p.M * N;
+    for (int e = tid; e < (int)p.M * COLS; e += NTHREADS) {
+      const int m = e / COLS, c = e - m * COLS;
+      if ((uint32_t)c < rows_wg) {
+        float base = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) base += red[((w * TILES + (c >> 4)) * 16 + m) * 16 + (c & 15)];
+        put_tagged(yp + (size_t)m * N + n0 + c, base, p.epoch);
       }
     }
-    __syncthreads();
+    return;
+  }
+  // The last part waits for T (the partials of workgroups 0..tunits-1,
+  // written early in this kernel, or of the separate k_tpart launch) and for
+  // the other parts of its columns.  Every workgroup it waits for has a lower
+  // index and waits for nothing itself.  The wait is bounded: a producer that
+  // never reports poisons this workgroup's output with NaN instead of hanging.
+  // The other parts' sums of this thread's outputs, all loads in flight at once:
+  constexpr int EPT = (16 * COLS + NTHREADS - 1) / NTHREADS;
+  constexpr int NQ = EPT * (MAX_KPARTS - 1);
+  uint64_t yq[NQ];
+  const uint64_t* yq_src[NQ];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + i * NTHREADS, m = e / COLS, c = e - m * COLS;
+    const bool ok = e < (int)p.M * COLS && (uint32_t)c < rows_wg;
+#pragma unroll
+    for (int q = 0; q < MAX_KPARTS - 1; ++q) {
+      const bool live = ok && q < p.kparts - 1;
+      yq_src[i * (MAX_KPARTS - 1) + q] = p.ypart + ((size_t)q * p.M + (live ? m : 0)) * N + n0 + (live ? c : 0);
+      yq[i * (MAX_KPARTS - 1) + q] = live ? get_tagged(yq_src[i * (MAX_KPARTS - 1) + q]) : (uint64_t)p.epoch << 32;
+    }
   }
   {
-    // T = the partials summed in split order (all loads of an element in
-    // flight at once); rows m >= M are zero
+    // T = the partials summed in split order; rows m >= M are zero
     for (int e = tid; e < 16 * r; e += NTHREADS) {
-      float pv[MAX_SPLIT];
+      uint64_t pv[MAX_SPLIT];
+      const uint64_t* src[MAX_SPLIT];
 #pragma unroll
-      for (int sp = 0; sp < MAX_SPLIT; ++sp)
-        pv[sp] = sp < p.nsplit ? __hip_atomic_load(p.tpart + sp * 16 * r + e, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : 0.0f;
+      for (int sp = 0; sp < MAX_SPLIT; ++sp) {
+        src[sp] = p.tpart + (sp < p.nsplit ? sp : 0) * 16 * r + e;
+        pv[sp] = sp < p.nsplit ? get_tagged_cached(src[sp]) : (uint64_t)p.epoch << 32;
+      }
+      if (!await_tagged(pv, src, p.nsplit, p.epoch)) s_bad = 1;
       float v = 0.0f;
 #pragma unroll
       for (int sp = 0; sp < MAX_SPLIT; ++sp)
-        if (sp < p.nsplit) v += pv[sp];
+        if (sp < p.nsplit) v += __uint_as_float((uint32_t)pv[sp]);
       ttab[e] = v;
-      if (blockIdx.x == 0 && e < (int)p.M * r) p.T_save[e] = v;
+      if (cg == 0 && e < (int)p.M * r) p.T_save[e] = v;
     }
   }
+  if (!await_tagged(yq, yq_src, NQ, p.epoch)) s_bad = 1;
   __syncthreads();
   const bool bad = s_bad != 0;
   const u16* btab = reinterpret_cast<const u16*>(smem + L.btab);
-  constexpr int COLS = 16 * TILES;
-  for (int e = tid; e < (int)p.M * COLS; e += NTHREADS) {
-    const int m = e / COLS, c = e - m * COLS;
-    if ((uint32_t)c < rows_wg) {
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + i * NTHREADS, m = e / COLS, c = e - m * COLS;
+    if (e < (int)p.M * COLS && (uint32_t)c < rows_wg) {
+      // the parts in order, then this one's waves in order
       float base = 0.0f;
+#pragma unroll
+      for (int q = 0; q < MAX_KPARTS - 1; ++q)
+        if (q < p.kparts - 1) base += __uint_as_float((uint32_t)yq[i * (MAX_KPARTS - 1) + q]);
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) base += red[((w * TILES + (c >> 4)) * 16 + m) * 16 + (c & 15)];
       float lora = 0.0f;
@@ -487,7 +697,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
 template <int TILES>
 static hipError_t launch_one(const DecArgs& p, hipStream_t st) {
   const int nbk = (int)(p.w.K / 64);
-  const Lds L = lds_layout(TILES, nbk, p.r);
+  const Lds L = lds_layout(TILES, nbk, nbk / p.kparts, p.r);
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
@@ -495,7 +705,7 @@ static hipError_t launch_one(const DecArgs& p, hipStream_t st) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)MAX_DYN_LDS);
   });
   if (attr != hipSuccess) return attr;
-  const unsigned grid = (unsigned)((p.w.N + 16 * TILES - 1) / (16 * TILES));
+  const unsigned grid = (unsigned)(p.gcols * p.kparts);
   hipLaunchKernelGGL((k_decode<TILES>), dim3(grid), dim3(NTHREADS), L.total, st, p);
   return hipGetLastError();
 }
@@ -512,19 +722,37 @@ static int device_cus() {
   return cus;
 }
 
-// tiles per workgroup: the fewest that keep the grid within one workgroup per
-// compute unit (more tiles per workgroup share each X fragment more widely)
-static int pick_tiles(int64_t N, int64_t K, int r) {
-  const int64_t tiles = (N + 15) / 16;
-  const int64_t cus = device_cus();
-  int t = (int)std::min<int64_t>(MAX_TILES, std::max<int64_t>(1, (tiles + cus - 1) / cus));
-  while (t > 1 && lds_layout(t, (int)(K / 64), r).total > MAX_DYN_LDS) --t;
-  return t;
+// Shape of the weight stream: TILES 16-column tiles per workgroup and the
+// contraction cut into kparts parts.  The address unit of a compute unit is
+// what bounds the stream (a 16-byte load of codes or of X costs it the same
+// time), so the plan minimises the wave loads of the most loaded compute
+// unit: each pair of blocks costs one code load per tile plus four X loads,
+// shared by all the workgroup's tiles.  A part must cover a multiple of 16
+// blocks of every row, so that its scale segments are 16-byte aligned.
+struct Plan {
+  int tiles, kparts;
+};
+static bool part_ok(int64_t K, int kparts) { return kparts == 1 || (K / 64) % (16 * kparts) == 0; }
+static Plan plan(int64_t N, int64_t K, int r) {
+  const int64_t cus = device_cus(), nbk = K / 64, npair = (nbk + 1) / 2;
+  Plan best{1, 1};
+  int64_t best_cost = -1;
+  for (int kp = 1; kp <= MAX_KPARTS; kp *= 2) {
+    if (!part_ok(K, kp)) continue;
+    for (int t = 1; t <= MAX_TILES; ++t) {
+      if (lds_layout(t, (int)nbk, (int)(nbk / kp), r).total > MAX_DYN_LDS) continue;
+      const int64_t grid = (N + 16 * t - 1) / (16 * t) * kp;
+      // (+ a fixed charge per extra part for the hand-over of its sums)
+      const int64_t cost = (grid + cus - 1) / cus * ((npair + kp - 1) / kp) * (t + 4) + 64 * (kp - 1);
+      if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = Plan{t, kp}; }
+    }
+  }
+  return best;
 }
 
-// Per-call epochs for the T-unit flags: a process-wide counter starting at a
+// Per-call tags of the partial sums: a process-wide counter starting at a
 // random value (so a workspace left over from another process is unlikely to
-// hold a matching flag); 0 is skipped.
+// hold a matching tag); 0 is skipped.
 static uint32_t next_epoch() {
   static std::atomic<uint32_t> counter{0};
   static std::once_flag once;
@@ -551,45 +779,50 @@ static TSplit t_split(int64_t K) {
 
 }  // namespace dec
 
-// workspace: T partials [nsplit][16][r] fp32, then one 32-bit flag per T unit
-int64_t decode_workspace_elems(int64_t K, int r) {
+// workspace, in 64-bit tagged words: T partials [nsplit][16][r] | the parts'
+// sums [MAX_KPARTS - 1][M][N] when K allows more than one part
+static int64_t dec_ws_words(int64_t M, int64_t N, int64_t K, int r) {
   const dec::TSplit ts = dec::t_split(K);
-  return (int64_t)ts.nsplit * 16 * r + (int64_t)ts.nsplit * ((r + 15) / 16) + 64;
+  const int64_t extra = dec::part_ok(K, 2) ? dec::MAX_KPARTS - 1 : 0;
+  return (int64_t)ts.nsplit * 16 * r + extra * M * N;
 }
+
+int64_t decode_workspace_elems(int64_t M, int64_t N, int64_t K, int r) { return 2 * dec_ws_words(M, N, K, r); }
 
 bool decode_fits(int64_t M, const NF4View& w, int r) {
   const int64_t lim = (int64_t)1 << 31;
   if (!(M >= 1 && M <= 16 && w.N * w.K / 2 < lim && 16 * w.K * 2 < lim && (int64_t)r * w.K * 2 < lim &&
-        w.N * r * 2 < lim))
+        w.N * r * 2 < lim && (dec::MAX_KPARTS - 1) * M * w.N < lim))
     return false;
-  return dec::lds_layout(1, (int)(w.K / 64), r).total <= dec::MAX_DYN_LDS;
+  return dec::lds_layout(1, (int)(w.K / 64), (int)(w.K / 64), r).total <= dec::MAX_DYN_LDS;
 }
 
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st) {
   const dec::TSplit ts = dec::t_split(w.K);
-  const int tiles = dec::pick_tiles(w.N, w.K, r);
-  const int64_t grid = (w.N + 16 * tiles - 1) / (16 * tiles);
+  const dec::Plan pl = dec::plan(w.N, w.K, r);
+  const int64_t gcols = (w.N + 16 * pl.tiles - 1) / (16 * pl.tiles);
   const int units = ((r + 15) / 16) * ts.nsplit;
   dec::DecArgs p;
   p.X = X; p.M = M; p.w = w; p.A = A; p.B = B; p.r = r; p.s = s;
-  p.tpart = ws; p.nsplit = ts.nsplit; p.kchunk = ts.kchunk;
-  p.flags = reinterpret_cast<uint32_t*>(ws + (int64_t)ts.nsplit * 16 * r);
+  uint64_t* words = reinterpret_cast<uint64_t*>(ws);   // 16-byte aligned (checked by the caller)
+  p.tpart = words; p.nsplit = ts.nsplit; p.kchunk = ts.kchunk;
+  p.kparts = pl.kparts; p.gcols = (int)gcols;
+  p.ypart = words + (int64_t)ts.nsplit * 16 * r;
   p.Y = Y; p.T_save = T_save;
-  if (units <= grid) {
-    // the first workgroups compute the T partials themselves; a fresh epoch
-    // per call tells their flags from those a previous call left behind
-    p.tunits = units;
-    p.epoch = dec::next_epoch();
+  // a fresh tag per call tells this call's partial sums from those a
+  // previous call left in the workspace
+  p.epoch = dec::next_epoch();
+  if (units <= gcols * pl.kparts) {
+    p.tunits = units;   // the first workgroups compute the T partials themselves
   } else {
     p.tunits = 0;
-    p.epoch = 0;
     hipLaunchKernelGGL(dec::k_tpart, dim3((unsigned)((r + 15) / 16), (unsigned)ts.nsplit),
-                       dim3(64 * dec::TP_WAVES), 0, st, X, (int)M, (uint32_t)w.K, A, r, ts.kchunk, ws);
+                       dim3(64 * dec::TP_WAVES), 0, st, X, (int)M, (uint32_t)w.K, A, r, ts.kchunk, p.tpart, p.epoch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  switch (tiles) {
+  switch (pl.tiles) {
     case 1: return dec::launch_one<1>(p, st);
     case 2: return dec::launch_one<2>(p, st);
     case 3: return dec::launch_one<3>(p, st);

@@ -155,6 +155,12 @@ DECODE = [
     (28672, 1024, 1, 16, 32.0),     # seven column tiles per workgroup
     (40000, 256, 4, 24, 16.0),      # eight tiles per workgroup, more than one round
     (12000, 4096, 16, 16, 32.0),    # three tiles per workgroup
+    (4100, 4096, 9, 24, 16.0),      # three tiles, two parts, ragged last column group
+    (2000, 2048, 1, 8, 16.0),       # one tile, a single token
+    (6000, 8192, 16, 64, 16.0),     # three tiles, two parts, four rank tiles of T
+    (1024, 16384, 1, 16, 32.0),     # one tile, four parts, a single token
+    (3000, 16384, 9, 24, 16.0),     # three tiles, four parts, ragged last column group
+    (1001, 704, 5, 3, 16.0),        # odd N*r and N*K/64 % 16 != 0: partial chunks at both arrays' ends
 ]
 
 
