@@ -37,18 +37,22 @@
 // and X is loaded with the same permutation, which leaves each block's sum
 // unchanged.  Each wave issues the next batch's loads one tile at a time
 // between the tiles of the current batch, so that the per-CU address unit
-// (about 16 bytes a clock, shared by the code and X loads) works through them
-// while the wave computes instead of stalling its issue.
+// works through them while the wave computes instead of stalling its issue.
 //
-// The restored scales of the workgroup's blocks and the LoRA factor B of its
-// columns are put in LDS at the start, behind the first batch's loads; T
-// (summed from the partials in a fixed order; the first column group also
-// writes it to T_save) at the end.  The eight waves' results are summed in
-// LDS in wave order, so results do not depend on timing.  Producers (T
-// units, parts other than the last) publish each sum as one coherent 64-bit
-// word tagged with a per-call epoch, which the consumer polls directly; they
-// have lower workgroup indices than every consumer and never wait, so the
-// waits always end.
+// Set-up data goes straight to LDS with direct-to-LDS loads issued before
+// the first two batches (loads complete in order, so waiting for the set-up
+// does not wait for the batches): each wave stages the 8-bit scales of its
+// own block pairs for every row of the workgroup and the (at most two)
+// second-level constants those blocks use, and restores each pair's scales
+// s = fl32(E4M3(q) * d) inside the loop with the hardware fp8 conversion;
+// the last part also stages the LoRA factor B of its columns.  T (summed
+// from the partials in a fixed order; the first column group also writes it
+// to T_save) is read at the end.  The eight waves' results are summed in LDS
+// in wave order, so results do not depend on timing.  Producers (T units,
+// parts other than the last) publish each sum as one coherent 64-bit word
+// tagged with a per-call epoch, which the consumer polls directly; they have
+// lower workgroup indices than every consumer and never wait, so the waits
+// always end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -105,6 +109,14 @@ template <int n>
 __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// A workgroup barrier after this thread's LDS writes have completed, with no
+// wait for its vector-memory loads (a plain __syncthreads would also wait for
+// the outstanding direct-to-LDS loads, which the barrier here does not need)
+__device__ __forceinline__ void barrier_lds_only() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
 }
 
 __device__ __forceinline__ void put_tagged(uint64_t* dst, float v, uint32_t epoch) {
@@ -188,53 +200,46 @@ __global__ __launch_bounds__(64 * TP_WAVES) void k_tpart(const u16* X, int M, ui
 // ---------------------------------------------------------------------------
 // Byte offsets of the dynamic LDS regions.  The same function runs on the
 // host (to size the launch) and on the device.  Regions that receive
-// direct-to-LDS loads are rounded up to what one wave's load instruction
-// writes (1 KB, or 256 bytes for 4-byte loads), so that the zeros written by
-// out-of-range lanes stay inside them.
+// direct-to-LDS loads are laid out in whole load instructions (64 lanes x 16
+// or 4 bytes), so that the zeros written by out-of-range lanes stay inside
+// them.
 struct Lds {
-  uint32_t btab, ttab, tred, stab, tstage, qstage, dstage, tails, red, total;
-  uint32_t spitch;                  // floats per row of the scale table
-  bool qalias;                      // the staged scale bytes lie inside the scale table
+  uint32_t btab, ttab, tred, qst, dst, tstage, tails, red, total;
+  uint32_t qb;                      // staged scale bytes per row and wave (a multiple of 16)
+  uint32_t rows_q, rows_d;          // row pitch of the scale-byte and dscale stages
 };
 __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1u) / a * a; }
-// nbk: 64-blocks per row of W; nbkp: the blocks of a row this workgroup covers
-__host__ __device__ inline Lds lds_layout(int tiles, int nbk, int nbkp, int r) {
+// ppw: the most block pairs a wave of the workgroup covers
+__host__ __device__ inline Lds lds_layout(int tiles, int ppw, int r) {
   Lds L;
   const uint32_t rows = 16u * (uint32_t)tiles;
-  // an even pitch of nbkp + 2 or more keeps 8-byte reads aligned and puts the
-  // 16 rows a wave reads at once in different banks
-  L.spitch = ((uint32_t)nbkp + 3u) & ~1u;
+  L.qb = align_up(2u * (uint32_t)(ppw > 0 ? ppw : 1), 16u);
+  L.rows_q = align_up(rows, 64u);
+  L.rows_d = align_up(rows, 32u);
   L.btab = 0;                                                    // B rows, bf16 [rows][r]
   L.ttab = align_up(L.btab + rows * (uint32_t)r * 2u, 1024u);    // T fp32 [16][r]
   L.tred = align_up(L.ttab + 16u * (uint32_t)r * 4u, 16u);       // a T unit's per-wave sums [8][256]
-  // overlay: restored block scales fp32 [rows][spitch]; before them a T
-  // unit's staged operands [8 waves][4][1 KB] at its start and the raw scale
-  // bytes (16 per chunk) at its end, when all of those fit in two chunks a
-  // thread (the fill reads them all before writing); after the loop the
-  // per-wave partial sums [8][tiles][1 KB]
-  L.stab = L.tred + (uint32_t)WAVES * 256u * 4u;
-  L.tstage = L.stab;
-  L.red = L.stab;
-  const uint32_t sbytes = rows * L.spitch * 4u, tbytes = (uint32_t)WAVES * 4096u;
-  const uint32_t nch = (rows * (uint32_t)nbkp + 15u) / 16u;
-  const uint32_t qsz = align_up(16u * nch, 1024u);
-  L.qalias = nch <= 2u * NTHREADS;
-  if (L.qalias) {
-    const uint32_t ov = align_up(sbytes > tbytes + qsz ? sbytes : tbytes + qsz, 16u);
-    L.qstage = L.stab + ov - qsz;
-    L.dstage = L.stab + ov;
-  } else {
-    const uint32_t ov = align_up(sbytes > tbytes ? sbytes : tbytes, 16u);
-    L.qstage = L.stab + ov;
-    L.dstage = L.qstage + qsz;
-  }
-  const uint32_t ngr = ((rows - 1u) * (uint32_t)nbk + (uint32_t)nbkp + 255u) / 256u + 2u;
-  L.tails = L.dstage + align_up(4u * ngr, 256u);                 // 2 x 64 dwords: end-of-array bytes
-  const uint32_t end_s = L.tails + 512u;
+  // until the loop ends: per wave, the 8-bit scales of its block pairs for
+  // every row ([qb / 16][rows_q][16 bytes]) and the two dscale values its
+  // rows can touch ([rows_d][2] fp32); a T unit's staged operands [8][4][1 KB];
+  // the last elements of B.  After the loop: the per-wave partial sums
+  // [8][tiles][1 KB].
+  L.qst = L.tred + (uint32_t)WAVES * 256u * 4u;
+  L.dst = L.qst + (uint32_t)WAVES * L.qb * L.rows_q;
+  L.tstage = L.dst + (uint32_t)WAVES * L.rows_d * 8u;
+  L.tails = L.tstage + (uint32_t)WAVES * 4096u;                  // 64 dwords
+  L.red = L.qst;
+  const uint32_t end_s = L.tails + 256u;
   const uint32_t end_r = L.red + (uint32_t)(WAVES * tiles) * 1024u;
   L.total = end_s > end_r ? end_s : end_r;
   return L;
 }
+
+// The split of a part's block pairs over the waves: wave w takes pairs
+// [wp0 + 2 floor(w h / 8), wp0 + 2 floor((w + 1) h / 8)) of the part's
+// [wp0, wp1), h = ceil((wp1 - wp0) / 2), so that every wave starts on an
+// even pair (its first scale byte is then 4-byte aligned).
+__host__ __device__ inline int wave_pairs_max(int npp) { return 2 * (((npp + 1) / 2 + WAVES - 1) / WAVES); }
 
 // TILES: 16-column tiles per workgroup.  One batch = NP pairs of blocks.
 template <int TILES>
@@ -256,15 +261,15 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   const uint32_t rows_wg = min((uint32_t)ROWS, N - n0);
   const bool last = kp == p.kparts - 1;
   const int wp0 = kp * npair / p.kparts, wp1 = (kp + 1) * npair / p.kparts;   // this part's pairs
-  const int kb0 = 2 * wp0, nbkp = min(nbk, 2 * wp1) - kb0;                    // and blocks
   const int r = p.r;
-  const Lds L = lds_layout(TILES, nbk, nbkp, r);
+  const Lds L = lds_layout(TILES, wave_pairs_max(wp1 - wp0), r);
 
   const auto rX = rsrc(p.X, (uint32_t)p.M * K * 2u);
   const auto rC = rsrc(p.w.codes, N * RB);
   const uint32_t nb_all = N * (uint32_t)nbk;
   const auto rQ = rsrc(p.w.qscale, nb_all);
-  const auto rD = rsrc(p.w.dscale, 4u * ((nb_all + 255u) / 256u));
+  const uint32_t ng = (nb_all + 255u) / 256u;
+  const auto rD = rsrc(p.w.dscale, 4u * ng);
   const auto rB = rsrc(p.B, N * (uint32_t)r * 2u);
 
   // this wave's pairs of blocks (computed from the wave index as a scalar,
@@ -272,7 +277,8 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   // without branching), and the per-lane load offsets
   const int wsc = __builtin_amdgcn_readfirstlane(wave);
   const int wv = (wsc + (int)blockIdx.x) & (WAVES - 1);
-  const int p0 = wp0 + wv * (wp1 - wp0) / WAVES, p1 = wp0 + (wv + 1) * (wp1 - wp0) / WAVES;
+  const int hp = (wp1 - wp0 + 1) / 2;
+  const int p0 = wp0 + 2 * (wv * hp / WAVES), p1 = min(wp1, wp0 + 2 * ((wv + 1) * hp / WAVES));
   uint32_t crow[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) crow[t] = (n0 + 16u * t + (uint32_t)i16) * RB + 16u * (uint32_t)g;
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
 
   typedef __attribute__((address_space(3))) void* lds_ptr;
 
-  // ---- tables that need no loads ----
+  // ---- the lookup table (no loads) ----
   {
     // word e holds the pair (byte & 15, byte >> 4) of byte e / 64: thread tid
     // writes bytes tid/64 + 8i, whose low nibble is tid/64 or tid/64 + 8
@@ -317,12 +323,11 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     for (int i = 0; i < 32; ++i)
       lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, __uint_as_float(kNF4LevelBits[i >> 1]));
   }
-  float* stab = reinterpret_cast<float*>(smem + L.stab);
   float* ttab = reinterpret_cast<float*>(smem + L.ttab);
 
-  // ---- set-up loads, issued before the first batch and written straight
+  // ---- set-up loads, issued before the first batches and written straight
   //      to LDS: loads complete in order, so that waiting for these does not
-  //      wait for the batch, and no register is tied up by them ----
+  //      wait for the batches, and no register is tied up by them ----
   // (a) a T unit's first two contraction steps: the partial T of rank tile tq
   //     over contraction split tsp; lane (i16, g) stages 16 bytes of X row i16
   //     and of A row 16 tq + i16, as its MFMA operands
@@ -361,52 +366,41 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(smem + L.tails), 2,
                                              (uint32_t)lane < btail ? bgoff + 16u * bnch + 2u * (uint32_t)lane : OOB,
                                              0, 0, 0);
-  // (c) the raw 8-bit scales of this workgroup's blocks, 16 per chunk: with
-  //     one part the blocks [q0, q0 + rows_wg * nbk) are contiguous; with more,
-  //     each row holds a segment of nbkp blocks (a multiple of 16, 16-byte
-  //     aligned).  Chunk c is staged at qstage + 16 c, so staged byte f is
-  //     block (f / nbkp, f % nbkp) of the workgroup's rows in both cases.
-  //     Chunks wholly inside the qscale array come straight to LDS; the bytes
-  //     of a last, partial one (at the end of the array only) come as one
-  //     byte load a lane, written as a dword to the tails area.
-  const bool flat = p.kparts == 1;
-  const uint32_t q0 = n0 * (uint32_t)nbk, qlen = rows_wg * (uint32_t)nbkp;
-  const uint32_t cpr = (uint32_t)nbkp / 16u;   // chunks per row segment (parts > 1)
-  const uint32_t nch = (qlen + 15u) / 16u;
-  auto chunk_at = [&](uint32_t c, uint32_t& lr, uint32_t& b, uint32_t& qoff) {
-    if (flat) { const uint32_t f0 = 16u * c; lr = f0 / (uint32_t)nbk; b = f0 - lr * (uint32_t)nbk; qoff = q0 + f0; }
-    else { lr = c / cpr; b = 16u * (c - lr * cpr); qoff = (n0 + lr) * (uint32_t)nbk + (uint32_t)kb0 + b; }
-  };
-  const uint32_t nch_dma = flat ? min(nch, (nb_all - q0) / 16u) : nch;
-  for (uint32_t u = (uint32_t)wsc; 64u * u < nch_dma; u += WAVES) {
-    const uint32_t c = 64u * u + (uint32_t)lane;
-    uint32_t lr, b, qoff;
-    chunk_at(c, lr, b, qoff);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr)(smem + L.qstage + 1024u * u), 16, c < nch_dma ? qoff : OOB,
-                                             0, 0, 0);
+  // (c) this wave's own scales: the 8-bit scales of its pairs for every row of
+  //     the workgroup (row R, chunk h of 16 bytes at [h][R]), and for every row
+  //     the dscale of the group holding the wave's first block and of the next
+  //     group (a wave covers at most 256 blocks, so at most two groups).  K is
+  //     a multiple of 256 and the wave starts on an even pair, so every scale
+  //     load is 4-byte aligned and a dword that holds a wanted byte lies
+  //     wholly inside the array.
+  uint8_t* qst = smem + L.qst + (uint32_t)wsc * L.qb * L.rows_q;
+  const float* dst = reinterpret_cast<const float*>(smem + L.dst + (uint32_t)wsc * L.rows_d * 8u);
+  for (uint32_t h = 0; 16u * h < L.qb; ++h) {
+#pragma unroll
+    for (int jr = 0; jr < (16 * TILES + 63) / 64; ++jr) {
+      const uint32_t R = 64u * jr + (uint32_t)lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr)(qst + (h * L.rows_q + 64u * jr) * 16u), 16,
+                                               R < rows_wg ? (n0 + R) * (uint32_t)nbk + 2u * (uint32_t)p0 + 16u * h
+                                                           : OOB,
+                                               0, 0, 0);
+    }
   }
-  const uint32_t qtail = qlen - min(qlen, 16u * nch_dma);   // < 16 bytes
-  if (wsc == 0 && qtail > 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr)(smem + L.tails + 256u), 1,
-                                             (uint32_t)lane < qtail ? q0 + 16u * nch_dma + (uint32_t)lane : OOB,
-                                             0, 0, 0);
-  // (d) the fp32 second-level constants of every group those blocks touch
-  const uint32_t gfirst = (flat ? q0 : q0 + (uint32_t)kb0) >> 8;
-  const uint32_t glast = (flat ? q0 + qlen - 1u : (n0 + rows_wg - 1u) * (uint32_t)nbk + (uint32_t)kb0 + (uint32_t)nbkp - 1u) >> 8;
-  const uint32_t ngr = glast - gfirst + 1u;
-  for (uint32_t u = (uint32_t)wsc; 64u * u < ngr; u += WAVES) {
-    const uint32_t gi = 64u * u + (uint32_t)lane;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_ptr)(smem + L.dstage + 256u * u), 4,
-                                             gi < ngr ? 4u * (gfirst + gi) : OOB, 0, 0, 0);
+#pragma unroll
+  for (int jr = 0; jr < (32 * TILES + 63) / 64; ++jr) {
+    const uint32_t R = 32u * jr + (uint32_t)(lane >> 1);
+    const uint32_t g0 = ((n0 + R) * (uint32_t)nbk + 2u * (uint32_t)p0) >> 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_ptr)(dst + 64 * jr), 4,
+                                             R < rows_wg ? 4u * (g0 + (uint32_t)(lane & 1)) : OOB, 0, 0, 0);
   }
 
   // the first two batches go out now, so that the memory system has work
-  // while the tables are built
+  // while the rest is set up
   Batch cur, nxt;
   __builtin_amdgcn_sched_barrier(0);   // keep every set-up load ahead of the batches
   load_batch(cur, p0);
   load_batch(nxt, p0 + NP);
   __builtin_amdgcn_sched_barrier(0);
+  barrier_lds_only();   // the lookup table is complete
   // the set-up loads are complete once no more than the two batches' loads
   // are outstanding
   wait_vm<2 * NP * (TILES + 4)>();
@@ -423,7 +417,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
         tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, av, tacc, 0, 0, 0);
       }
     }
-    // further steps (a split longer than 16 steps) load behind the batch
+    // further steps (a split longer than 16 steps) load behind the batches
     if (tk1 - tk0 > 64u * WAVES) {
       for (uint32_t kk = tk0 + 32u * (uint32_t)(wave + 2 * WAVES); kk < tk1; kk += 32u * WAVES * 2) {
         const uint32_t ka = kk, kb = kk + 32u * WAVES;
@@ -446,76 +440,26 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       if (j < r) put_tagged(p.tpart + ((size_t)tsp * 16 + m) * r + j, v, p.epoch);
     }
   }
-  // wave 0 moves the end-of-array elements it staged into place; then every
-  // wave's staged data is in LDS (and a T unit is done with its staging
-  // area, which the scale table overwrites)
+  // wave 0 moves the last elements of B it staged into place (read in the
+  // epilogue, after barriers)
   {
     const uint32_t* tl = reinterpret_cast<const uint32_t*>(smem + L.tails);
     if ((uint32_t)tid < btail) reinterpret_cast<uint16_t*>(smem + L.btab)[8u * bnch + (uint32_t)tid] = (uint16_t)tl[tid];
-    if ((uint32_t)tid < qtail) (smem + L.qstage)[16u * nch_dma + (uint32_t)tid] = (uint8_t)tl[64 + tid];
   }
-  __syncthreads();
 
-  // ---- the restored scales s_b = fl32(E4M3(q_b) * d_g), from the staged bytes ----
-  {
-    // A chunk is 16 blocks at a 16-aligned position of the qscale array, so
-    // it lies in one group of 256 (one d_g); when nbkp is a multiple of 16 it
-    // also lies in one row.  E4M3 is decoded by the hardware conversion (OCP
-    // E4M3FN on this target, exact).
-    const float* dst = reinterpret_cast<const float*>(smem + L.dstage);
-    const bool in_row = (nbkp & 15) == 0;
-    auto fill_chunk = [&](uint32_t c, const u32x4v& v) {
-      uint32_t lr, b, qoff;
-      chunk_at(c, lr, b, qoff);
-      const float d = dst[(qoff >> 8) - gfirst];
-      float f[16];
+  // per tile, this lane's row: its two dscale values and the first block
+  // (relative to the row) that lies in the second group
+  float d0[TILES], d1[TILES];
+  int kb_sw[TILES];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
-        f[4 * w] = lo[0] * d;
-        f[4 * w + 1] = lo[1] * d;
-        f[4 * w + 2] = hi[0] * d;
-        f[4 * w + 3] = hi[1] * d;
-      }
-      if (in_row) {
-        float* row = stab + lr * L.spitch + b;   // 8-byte aligned: even pitch, b a multiple of 16
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x2v*>(row + 2 * j) = f32x2v{f[2 * j], f[2 * j + 1]};
-      } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          if (16u * c + k < qlen) stab[lr * L.spitch + b] = f[k];
-          if (++b == (uint32_t)nbkp) { b = 0; ++lr; }
-        }
-      }
-    };
-    // the scale table's padding (columns past nbkp, rows past this
-    // workgroup's last row) is read by dead pairs and must be finite
-    auto zero_padding = [&]() {
-      for (int lr = tid; lr < ROWS; lr += NTHREADS)
-        for (uint32_t b = (uint32_t)nbkp; b < L.spitch; ++b) stab[lr * L.spitch + b] = 0.0f;
-      for (uint32_t e = (uint32_t)tid; e < ((uint32_t)ROWS - rows_wg) * L.spitch; e += NTHREADS)
-        stab[rows_wg * L.spitch + e] = 0.0f;
-    };
-    const uint8_t* qst = smem + L.qstage;
-    if (L.qalias) {
-      // the staged bytes share the table's space: read them all first
-      const uint32_t c0 = (uint32_t)tid, c1 = c0 + NTHREADS;
-      u32x4v v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-      if (c0 < nch) v0 = *reinterpret_cast<const u32x4v*>(qst + 16u * c0);
-      if (c1 < nch) v1 = *reinterpret_cast<const u32x4v*>(qst + 16u * c1);
-      __syncthreads();
-      zero_padding();
-      if (c0 < nch) fill_chunk(c0, v0);
-      if (c1 < nch) fill_chunk(c1, v1);
-    } else {
-      zero_padding();
-      for (uint32_t c = (uint32_t)tid; c < nch; c += NTHREADS)
-        fill_chunk(c, *reinterpret_cast<const u32x4v*>(qst + 16u * c));
-    }
+  for (int t = 0; t < TILES; ++t) {
+    const uint32_t R = 16u * t + (uint32_t)i16;
+    const f32x2v dd = *reinterpret_cast<const f32x2v*>(dst + 2 * R);
+    d0[t] = dd.x;
+    d1[t] = dd.y;
+    const uint32_t rb = (n0 + R) * (uint32_t)nbk;
+    kb_sw[t] = (int)(256u * (((rb + 2u * (uint32_t)p0) >> 8) + 1u) - rb);
   }
-  __syncthreads();
 
   // LDS address of (code byte e of word c, this lane's copy) = byte << 8 | lane * 4,
   // assembled by one byte permute
@@ -537,7 +481,9 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     for (int u = 0; u < NP; ++u) {
       // a pair past the row's end (the last batch of a wave may hold one) has
       // zero X; any finite scale then adds nothing
-      const int prs = min(pr0 + u, wp1 - 1);
+      const int prs = min(pr0 + u, p1 - 1);
+      const int jb = 2 * (prs - p0);   // the pair's first scale byte in the wave's stage
+      const uint32_t qoff = (uint32_t)((jb >> 4) * (int)L.rows_q * 16 + (jb & 15));
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         if constexpr (decltype(prefetch)::value) load_slot(nb, pr0 + NP, u, t);
@@ -546,7 +492,11 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
         const auto s02 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].x, bt.c[u][t].z, false, false);
         const auto s13 = __builtin_amdgcn_permlane32_swap(bt.c[u][t].y, bt.c[u][t].w, false, false);
         const uint32_t w[4] = {s02[0], s13[0], s02[1], s13[1]};
-        const f32x2v sc = *reinterpret_cast<const f32x2v*>(stab + (16 * t + i16) * L.spitch + 2 * (prs - wp0));
+        // restored scales s = fl32(E4M3(q) * d) of blocks 2 prs and 2 prs + 1 of this lane's row
+        const uint32_t q2 = *reinterpret_cast<const uint16_t*>(qst + (16u * t + (uint32_t)i16) * 16u + qoff);
+        const auto e2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q2, false);
+        const f32x2v sc = {e2[0] * (2 * prs < kb_sw[t] ? d0[t] : d1[t]),
+                           e2[1] * (2 * prs + 1 < kb_sw[t] ? d0[t] : d1[t])};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4v wa = {lookup(w[2 * h], 0), lookup(w[2 * h], 1), lookup(w[2 * h], 2), lookup(w[2 * h], 3)};
@@ -587,7 +537,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   }
 
   // ---- cross-wave sums (fixed wave order), LoRA term, store ----
-  __syncthreads();   // every wave is done with the scale table
+  __syncthreads();   // every wave is done with its stages
   float* red = reinterpret_cast<float*>(smem + L.red);
   // slot layout [wave][tile][m][16]; lane (col i16, rows 4g..4g+3)
 #pragma unroll
@@ -697,7 +647,8 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
 template <int TILES>
 static hipError_t launch_one(const DecArgs& p, hipStream_t st) {
   const int nbk = (int)(p.w.K / 64);
-  const Lds L = lds_layout(TILES, nbk, nbk / p.kparts, p.r);
+  const int npair = (nbk + 1) / 2;
+  const Lds L = lds_layout(TILES, wave_pairs_max((npair + p.kparts - 1) / p.kparts), p.r);
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
@@ -735,12 +686,13 @@ struct Plan {
 static bool part_ok(int64_t K, int kparts) { return kparts == 1 || (K / 64) % (16 * kparts) == 0; }
 static Plan plan(int64_t N, int64_t K, int r) {
   const int64_t cus = device_cus(), nbk = K / 64, npair = (nbk + 1) / 2;
-  Plan best{1, 1};
+  Plan best{0, 0};
   int64_t best_cost = -1;
   for (int kp = 1; kp <= MAX_KPARTS; kp *= 2) {
     if (!part_ok(K, kp)) continue;
     for (int t = 1; t <= MAX_TILES; ++t) {
-      if (lds_layout(t, (int)nbk, (int)(nbk / kp), r).total > MAX_DYN_LDS) continue;
+      const int ppw = wave_pairs_max((int)((npair + kp - 1) / kp));
+      if (ppw > 128 || lds_layout(t, ppw, r).total > MAX_DYN_LDS) continue;   // a wave spans <= 2 groups
       const int64_t grid = (N + 16 * t - 1) / (16 * t) * kp;
       // (+ a fixed charge per extra part for the hand-over of its sums)
       const int64_t cost = (grid + cus - 1) / cus * ((npair + kp - 1) / kp) * (t + 4) + 64 * (kp - 1);
@@ -794,7 +746,8 @@ bool decode_fits(int64_t M, const NF4View& w, int r) {
   if (!(M >= 1 && M <= 16 && w.N * w.K / 2 < lim && 16 * w.K * 2 < lim && (int64_t)r * w.K * 2 < lim &&
         w.N * r * 2 < lim && (dec::MAX_KPARTS - 1) * M * w.N < lim))
     return false;
-  return dec::lds_layout(1, (int)(w.K / 64), (int)(w.K / 64), r).total <= dec::MAX_DYN_LDS;
+  // K a multiple of 256 keeps every wave's scale loads 4-byte aligned
+  return (w.K / 64) % 4 == 0 && dec::plan(w.N, w.K, r).tiles > 0;
 }
 
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,

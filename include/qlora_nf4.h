@@ -137,10 +137,11 @@ size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
  *   T_save[m][j] = sum_k X[m][k] A[j][k]                     fp32 [M][r]
  *   Y[m][n]      = bf16(sum_k X[m][k] W'[n][k] + s sum_j T[m][j] B[n][j])  [M][N]
  * with s = fl32(alpha / r); products of bf16 operands summed in fp32 (MFMA).
- * For M > 16 T enters the LoRA product as bf16(s T); for M <= 16 (the
- * HBM-bound decode path) the LoRA sum is fp32 and each 64-block's partial
- * dot product with bf16(L[code]) is scaled by the block scale in fp32, which
- * rounds the weight's relative value to bf16 once, as dequantization does.
+ * For M > 16 T enters the LoRA product as bf16(s T); for M <= 16 with K a
+ * multiple of 256 (the HBM-bound decode path) the LoRA sum is fp32 and each
+ * 64-block's partial dot product with bf16(L[code]) is scaled by the block
+ * scale in fp32, which rounds the weight's relative value to bf16 once, as
+ * dequantization does (other shapes take the M > 16 path).
  * X [M][K], A [r][K],
  * B [N][r] bf16 (device).  1 <= r <= QLORA_MAX_RANK.  compute_dtype must be
  * QL_DTYPE_BF16.  T_save (fp32, required) is the saved activation the

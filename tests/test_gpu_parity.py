@@ -160,7 +160,8 @@ DECODE = [
     (6000, 8192, 16, 64, 16.0),     # three tiles, two parts, four rank tiles of T
     (1024, 16384, 1, 16, 32.0),     # one tile, four parts, a single token
     (3000, 16384, 9, 24, 16.0),     # three tiles, four parts, ragged last column group
-    (1001, 704, 5, 3, 16.0),        # odd N*r and N*K/64 % 16 != 0: partial chunks at both arrays' ends
+    (1001, 768, 5, 3, 16.0),        # odd N*r: the last elements of B come apart from its 16-byte chunks
+    (1001, 704, 5, 3, 16.0),        # K % 256 != 0: the prefill kernels serve it
 ]
 
 
