@@ -223,6 +223,36 @@ def bench_decode(hip, reps=60):
     return out
 
 
+def bench_library_reference(hip, layers, reps=10):
+    """Context only, not part of the path: a dense bf16 matmul from the vendor
+    library (torch -> hipBLASLt) on the same shapes as the two fused forward
+    GEMMs, with random operands.  It bounds what a dense GEMM reaches on this
+    chip without any NF4 work; the fused kernels are compared with it."""
+    import torch
+    st = torch.cuda.current_stream().cuda_stream
+    out = []
+    g = torch.Generator(device="cuda").manual_seed(1)
+    for lay in layers:
+        X = torch.randn(lay.M, lay.K, device="cuda", dtype=torch.bfloat16, generator=g)
+        Wt = torch.randn(lay.K, lay.N, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+        Wt = Wt.contiguous()
+        for _ in range(3):
+            X @ Wt
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for _ in range(reps):
+            X @ Wt
+        hip.record(e1, st)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        fl = 2 * lay.M * lay.N * lay.K
+        out.append({"MxNxK": f"{lay.M}x{lay.N}x{lay.K}", "ms": round(ms, 4),
+                    "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1)})
+        del X, Wt
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_quantize(hip, layers, reps=20):
     import torch
     st = torch.cuda.current_stream().cuda_stream
@@ -394,6 +424,10 @@ def main():
         extras["quantize"] = bench_quantize(hip, layers)
         log("[bench] decode shapes")
         extras["decode"] = bench_decode(hip)
+
+    if not args.no_extras:
+        log("[bench] library reference")
+        extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
 
     cpu = None
     if not args.no_cpu_baseline:
