@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_qlora_adapter_entries.argtypes = [I64, I64, P, P, I64, P, P, I, D, I64, P, P, P,
                                                    I64, P, P, P, I]
         L.oracle_qlora_adapter_entries.restype = I
+        L.oracle_bf16_rne_double.argtypes = [D]
+        L.oracle_bf16_rne_double.restype = ctypes.c_uint16
+        L.oracle_lora_merge.argtypes = [P, I64, I64, P, P, I, D, I, P, I]
+        L.oracle_lora_merge.restype = I
         _lib = L
     return _lib
 
@@ -227,3 +231,23 @@ def qlora_adapter_entries(X, dY, A, B, alpha: float, dA_idx, dB_idx, threads: in
                                               threads or default_threads()),
            "qlora_adapter_entries")
     return oa, ob
+
+
+def bf16_rne_double(x: float) -> int:
+    """bf16 RNE of a double, rounded once."""
+    return int(lib().oracle_bf16_rne_double(float(x)))
+
+
+def lora_merge(W_base, A, B, alpha: float, sign: int = 1, threads: int | None = None):
+    """W_out = bf16(W_base + sign (alpha/r) B A), evaluated in double and rounded once
+    (IBM "What is LoRA?": the update B A folded into the weight; Ultralytics "QLoRA",
+    "Trade-offs": merging needs the base dequantized to 16 bit first).  W_base bf16 [N][K]
+    bits, A [r][K], B [N][r]; returns uint16 [N][K]."""
+    Wb, Ab, Bb = _u16(W_base), _u16(A), _u16(B)
+    N, K = Wb.shape
+    r = Ab.shape[0]
+    assert Ab.shape == (r, K) and Bb.shape == (N, r)
+    out = np.empty((N, K), np.uint16)
+    _check(lib().oracle_lora_merge(_ptr(Wb), N, K, _ptr(Ab), _ptr(Bb), r, float(alpha), int(sign), _ptr(out),
+                                   threads or default_threads()), "lora_merge")
+    return out

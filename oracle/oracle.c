@@ -508,3 +508,69 @@ int oracle_qlora_adapter_entries(int64_t N, int64_t K, const uint16_t* X, const 
   free(Ucol); free(Tcol); free(need_u); free(need_t);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* bf16 RNE of a double.  The candidates are the bf16 value whose pattern is  */
+/* the top half of the nearest float and its two neighbours of the same sign */
+/* (the exact value lies within one float step of that float, so it is       */
+/* bracketed by two of them); the nearest wins, ties go to the even pattern. */
+/* Past the largest finite bf16 the next step is 2^128 (IEEE overflow rule). */
+/* ------------------------------------------------------------------------ */
+static double bf16_value_for_rounding(uint16_t h) {
+  if ((h & 0x7FFF) == 0x7F80) return (h & 0x8000) ? -ldexp(1.0, 128) : ldexp(1.0, 128);
+  return bf16_to_double(h);
+}
+
+uint16_t oracle_bf16_rne_double(double x) {
+  if (isnan(x)) return 0x7FC0;
+  const uint16_t c = (uint16_t)(f2u((float)x) >> 16);
+  const uint16_t sign = c & 0x8000, mag = c & 0x7FFF;
+  uint16_t cand[3];
+  int n = 0;
+  if (mag > 0) cand[n++] = (uint16_t)(sign | (mag - 1));
+  cand[n++] = c;
+  if (mag < 0x7F80) cand[n++] = (uint16_t)(sign | (mag + 1));
+  uint16_t best = cand[0];
+  double bd = fabs(bf16_value_for_rounding(cand[0]) - x);
+  for (int i = 1; i < n; ++i) {
+    const double d = fabs(bf16_value_for_rounding(cand[i]) - x);
+    if (d < bd || (d == bd && (cand[i] & 1) == 0)) { best = cand[i]; bd = d; }
+  }
+  /* a finite x never rounds to a value of the other sign, and zero keeps x's sign */
+  if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+  return best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Merge / unmerge (IBM "What is LoRA?"; Ultralytics "QLoRA", "Trade-offs"):  */
+/* W_out = bf16(W_base + sign (alpha/r) B A), one rounding per element.       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const uint16_t* W; int64_t N, K; const uint16_t* A; const uint16_t* B; int r; double s;
+  uint16_t* out;
+} merge_ctx;
+
+static void merge_range(void* p, int64_t n0, int64_t n1) {
+  merge_ctx* c = (merge_ctx*)p;
+  double* row = (double*)malloc((size_t)c->K * sizeof(double));
+  for (int64_t n = n0; n < n1; ++n) {
+    for (int64_t k = 0; k < c->K; ++k) row[k] = 0.0;
+    for (int j = 0; j < c->r; ++j) {
+      const double b = bf16_to_double(c->B[n * c->r + j]);
+      const uint16_t* a = c->A + (int64_t)j * c->K;
+      for (int64_t k = 0; k < c->K; ++k) row[k] += b * bf16_to_double(a[k]);
+    }
+    for (int64_t k = 0; k < c->K; ++k)
+      c->out[n * c->K + k] = oracle_bf16_rne_double(bf16_to_double(c->W[n * c->K + k]) + c->s * row[k]);
+  }
+  free(row);
+}
+
+int oracle_lora_merge(const uint16_t* W_base, int64_t N, int64_t K, const uint16_t* A,
+                      const uint16_t* B, int r, double alpha, int sign, uint16_t* W_out,
+                      int nthreads) {
+  if (!W_base || !A || !B || !W_out || N <= 0 || K <= 0 || r <= 0 || (sign != 1 && sign != -1)) return -1;
+  merge_ctx c = { W_base, N, K, A, B, r, (double)sign * alpha / (double)r, W_out };
+  parallel_for(N, nthreads, merge_range, &c);
+  return 0;
+}

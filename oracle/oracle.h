@@ -111,6 +111,22 @@ int oracle_qlora_adapter_entries(int64_t N, int64_t K, const uint16_t* X, const 
                                  const int64_t* dB_n, const int64_t* dB_j, double* dB_out,
                                  int nthreads);
 
+/* bf16 RNE of a double, rounded once (no intermediate float rounding). */
+uint16_t oracle_bf16_rne_double(double x);
+
+/* The adapter folded into the frozen weight.  IBM "What is LoRA?": once
+ * training ends the low-rank update B A is merged into the pretrained weight
+ * matrix, which adds no inference latency, and adapters are swapped by task;
+ * Ultralytics "QLoRA", "Trade-offs": the merge needs the base dequantized to
+ * 16 bit first.
+ *   W_out[n][k] = bf16_RNE( W_base[n][k] + sign (alpha/r) sum_j B[n][j] A[j][k] )
+ * evaluated in double and rounded once.  W_base bf16 [N][K] is the dequantized
+ * NF4 weight (merge, sign = +1) or a merged weight (unmerge, sign = -1).
+ * A [r][K], B [N][r] bf16.  W_out may equal W_base. */
+int oracle_lora_merge(const uint16_t* W_base, int64_t N, int64_t K, const uint16_t* A,
+                      const uint16_t* B, int r, double alpha, int sign, uint16_t* W_out,
+                      int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -415,3 +415,95 @@ def test_adapter_entries_match_full_adapters(orc):
     ea, eb = orc.qlora_adapter_entries(X, dY, A, B, cfg.alpha, ia, ib)
     assert np.array_equal(ea, np.array([dA[j, k] for j, k in ia]))
     assert np.array_equal(eb, np.array([dB[n, j] for n, j in ib]))
+
+
+# --------------------------------------------------------------------------
+# f1: the adapter merged into the weight (IBM "What is LoRA?"; Ultralytics
+# "QLoRA", "Trade-offs"), and the double -> bf16 rounding it uses
+# --------------------------------------------------------------------------
+def test_bf16_rne_double_rounds_once(orc):
+    """Doubles that are floats round as the float rounding (pinned against
+    torch above); values a hair off a tie, closer than a float can express,
+    round by the exact rule, which a float intermediate would get wrong."""
+    rng = np.random.default_rng(21)
+    u = rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]
+    for x in u.view(np.float32)[:5000]:
+        assert orc.bf16_rne_double(float(x)) == orc.bf16_rne(float(x))
+    one = 0x3F80
+    assert orc.bf16_rne_double(1.0 + 2.0**-8) == one                 # tie -> even (1.0)
+    assert orc.bf16_rne_double(1.0 + 2.0**-8 + 2.0**-40) == one + 1  # just above the tie
+    assert orc.bf16_rne_double(1.0 + 3 * 2.0**-8) == one + 2          # tie -> even (1 + 2^-6)
+    assert orc.bf16_rne_double(1.0 + 3 * 2.0**-8 - 2.0**-40) == one + 1
+    assert orc.bf16_rne_double(-(1.0 + 2.0**-8 + 2.0**-40)) == 0x8000 | (one + 1)
+    assert orc.bf16_rne_double(0.0) == 0x0000 and orc.bf16_rne_double(-0.0) == 0x8000
+    big = float(np.float32(3.3895314e38))                              # largest finite bf16
+    assert orc.bf16_rne_double(big) == 0x7F7F
+    assert orc.bf16_rne_double(2.0**128) == 0x7F80                    # overflow -> inf
+
+
+def _merge_problem(orc, N=40, K=192, M=6, r=5, alpha=10.0, seed=4):
+    cfg, Wdq, X, A, B, dY = _small_problem(orc, N=N, K=K, M=M, r=r, alpha=alpha, seed=seed)
+    return cfg, Wdq, X, A, B
+
+
+def _ulp_bf16(v):
+    """Spacing of bf16 at |v| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0**-126)))
+    return 2.0 ** (e - 7)
+
+
+def test_merge_with_zero_B_is_the_dequantized_weight(orc):
+    cfg, Wdq, X, A, B = _merge_problem(orc)
+    Bz = np.zeros_like(B)
+    assert np.array_equal(orc.lora_merge(Wdq, A, Bz, cfg.alpha), Wdq)
+    assert np.array_equal(orc.lora_merge(Wdq, A, B, 0.0), Wdq)
+
+
+def test_merged_weight_reproduces_the_forward(orc):
+    """X bf16(W' + s B A)^T equals the forward oracle's Y up to the one bf16
+    rounding per weight; the adapter's share is far above that rounding, so a
+    wrong sign, scale or operand order fails."""
+    cfg, Wdq, X, A, B = _merge_problem(orc)
+    Wm = orc.lora_merge(Wdq, A, B, cfg.alpha)
+    Y, _ = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha)
+    Ym = _f(X) @ _f(Wm).T
+    bound = np.abs(_f(X)) @ (np.abs(_f(Wm)) * 2.0**-8).T
+    assert np.all(np.abs(Ym - Y) <= bound + 1e-300)
+    Y0, _ = orc.qlora_fwd(Wdq, X, A, B, 0.0)
+    assert np.max(np.abs(Y - Y0)) > 20 * np.max(bound)                # the adapter matters here
+
+
+def test_unmerge_inverts_merge(orc):
+    cfg, Wdq, X, A, B = _merge_problem(orc)
+    Wm = orc.lora_merge(Wdq, A, B, cfg.alpha)
+    Wu = orc.lora_merge(Wm, A, B, cfg.alpha, sign=-1)
+    d = np.abs(_f(Wu) - _f(Wdq))
+    assert np.all(d <= 0.5 * (_ulp_bf16(_f(Wm)) + _ulp_bf16(_f(Wu))) + 1e-300)
+    assert np.mean(Wu == Wdq) > 0.5
+    assert not np.array_equal(Wm, Wdq)
+
+
+def test_merge_does_not_depend_on_thread_count(orc):
+    cfg, Wdq, X, A, B = _merge_problem(orc, N=33, K=128, r=3)
+    assert np.array_equal(orc.lora_merge(Wdq, A, B, cfg.alpha, threads=1),
+                          orc.lora_merge(Wdq, A, B, cfg.alpha, threads=7))
+
+
+def test_merge_is_exact_on_small_integers(orc):
+    """With integer base, adapters and s = alpha/r = 2, W + s B A is an integer
+    below 2^8, so bf16 holds it exactly: the merge must equal the integer
+    product (numpy) bit for bit.  This fixes the scale, sign and operand order
+    exactly, beyond what a rounding bound can."""
+    rng = np.random.default_rng(8)
+    N, K, r, alpha = 24, 64, 5, 10.0
+    Wi = rng.integers(-40, 41, (N, K))
+    Ai = rng.integers(-2, 3, (r, K))
+    Bi = rng.integers(-2, 3, (N, r))
+    exact = Wi + 2 * (Bi @ Ai)
+    assert np.max(np.abs(exact)) < 256
+    bits = lambda a: si.to_bf16_bits(a.astype(np.float32))
+    got = orc.lora_merge(bits(Wi), bits(Ai), bits(Bi), alpha)
+    assert np.array_equal(got, bits(exact))
+    back = orc.lora_merge(got, bits(Ai), bits(Bi), alpha, sign=-1)
+    assert np.array_equal(back, bits(Wi))
