@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_workspace_bytes.restype = SZ
     L.qlora_linear_bwd.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P, SZ, P]
     L.qlora_linear_bwd.restype = I
+    L.qlora_merge.argtypes = [WP, P, P, I, F, P, P]
+    L.qlora_merge.restype = I
+    L.qlora_unmerge.argtypes = [P, I64, I64, P, P, I, F, P, P]
+    L.qlora_unmerge.restype = I
     L.qlora_set_timing_events.argtypes = [P, P, P, P]
     L.qlora_set_timing_events.restype = I
     _lib = L
@@ -162,6 +166,37 @@ def nf4_dequantize(w: NF4Weight, out=None, stream=None):
     _need(out, torch.bfloat16, (w.rows, w.cols), "out")
     d = w.descriptor()
     _check(lib().nf4_dequantize(ctypes.byref(d), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def qlora_merge(w: NF4Weight, A, B, alpha: float, out=None, stream=None):
+    """bf16 [rows, cols] = bf16(W' + (alpha/r) B A): the adapter merged into the weight."""
+    import torch
+    r = A.shape[0]
+    _need(A, torch.bfloat16, (r, w.cols), "A")
+    _need(B, torch.bfloat16, (w.rows, r), "B")
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.codes.device)
+    _need(out, torch.bfloat16, (w.rows, w.cols), "out")
+    d = w.descriptor()
+    _check(lib().qlora_merge(ctypes.byref(d), A.data_ptr(), B.data_ptr(), r, float(alpha),
+                             out.data_ptr(), _stream(stream)))
+    return out
+
+
+def qlora_unmerge(W_merged, A, B, alpha: float, out=None, stream=None):
+    """bf16 [rows, cols] = bf16(W_merged - (alpha/r) B A); out may be W_merged (in place)."""
+    import torch
+    rows, cols = W_merged.shape
+    r = A.shape[0]
+    _need(W_merged, torch.bfloat16, (rows, cols), "W_merged")
+    _need(A, torch.bfloat16, (r, cols), "A")
+    _need(B, torch.bfloat16, (rows, r), "B")
+    if out is None:
+        out = torch.empty_like(W_merged)
+    _need(out, torch.bfloat16, (rows, cols), "out")
+    _check(lib().qlora_unmerge(W_merged.data_ptr(), rows, cols, A.data_ptr(), B.data_ptr(), r, float(alpha),
+                               out.data_ptr(), _stream(stream)))
     return out
 
 

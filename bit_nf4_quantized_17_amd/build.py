@@ -24,6 +24,7 @@ SOURCES = {
     "gemm.hip": [],
     "gemm_big.hip": [],
     "decode.hip": [],
+    "merge.hip": [],
     "capi.hip": [],
 }
 

@@ -170,6 +170,33 @@ int nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, void* stream) {
   return hip_status(launch_dequantize(view(w), W_bf16, (hipStream_t)stream), "nf4_dequantize launch");
 }
 
+int qlora_merge(const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                uint16_t* W_out, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (r < 1 || r > QLORA_MAX_RANK) return fail(QL_ERR_UNSUPPORTED, "r=%d outside [1, %d]", r, QLORA_MAX_RANK);
+  if (!A || !B || !W_out) return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(W_out))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (!merge_fits(w->rows, w->cols, r)) return fail(QL_ERR_SHAPE, "weight or adapter too large (32-bit offsets)");
+  return hip_status(launch_merge(view(w), A, B, r, alpha / (float)r, W_out, (hipStream_t)stream),
+                    "qlora_merge launch");
+}
+
+int qlora_unmerge(const uint16_t* W_merged, int64_t rows, int64_t cols, const uint16_t* A,
+                  const uint16_t* B, int r, float alpha, uint16_t* W_out, void* stream) {
+  if (rows <= 0 || cols <= 0 || cols % 8)
+    return fail(QL_ERR_SHAPE, "weight shape %lld x %lld (need positive, cols %% 8 == 0)", (long long)rows,
+                (long long)cols);
+  if (r < 1 || r > QLORA_MAX_RANK) return fail(QL_ERR_UNSUPPORTED, "r=%d outside [1, %d]", r, QLORA_MAX_RANK);
+  if (!W_merged || !A || !B || !W_out) return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(W_merged) || !aligned16(A) || !aligned16(B) || !aligned16(W_out))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (!merge_fits(rows, cols, r)) return fail(QL_ERR_SHAPE, "weight or adapter too large (32-bit offsets)");
+  return hip_status(launch_unmerge(W_merged, rows, cols, A, B, r, alpha / (float)r, W_out, (hipStream_t)stream),
+                    "qlora_unmerge launch");
+}
+
 size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QLORA_MAX_RANK) return 0;
   return fwd_ws(M, N, K, r);

@@ -85,6 +85,15 @@ hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const f
 // it and decode_workspace_elems how many fp32 elements of ws it needs.
 bool decode_fits(int64_t M, const NF4View& w, int r);
 int64_t decode_workspace_elems(int64_t M, int64_t N, int64_t K, int r);
+// Adapter merge / unmerge (merge.hip): out = bf16(base +/- s B A), base the
+// dequantized NF4 weight or a bf16 weight; merge_fits says whether the 32-bit
+// offsets hold for a shape.
+bool merge_fits(int64_t N, int64_t K, int r);
+hipError_t launch_merge(const NF4View& w, const u16* A, const u16* B, int r, float s, u16* out,
+                        hipStream_t st);
+hipError_t launch_unmerge(const u16* w_in, int64_t N, int64_t K, const u16* A, const u16* B, int r,
+                          float s, u16* out, hipStream_t st);
+
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st);
 

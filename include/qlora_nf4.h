@@ -177,6 +177,28 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
                      uint16_t* dX, uint16_t* dA, uint16_t* dB,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Merge the adapter into the weight (IBM "What is LoRA?": after training the
+ * low-rank update B A is merged into the pretrained weight, which then runs
+ * with no extra inference latency; Ultralytics "QLoRA", "Trade-offs": the
+ * merge needs the base dequantized to 16 bit first):
+ *   W_out[n][k] = bf16_RNE( fl32(W'[n][k]) + s * sum_j B[n][j] A[j][k] ),
+ * s = fl32(alpha / r), W' the bf16 dequantized weight (nf4_dequantize), the
+ * rank-r sum in fp32 from bf16 products, base and product combined with one
+ * fused multiply-add.  A [r][K], B [N][r] bf16 (device); W_out bf16 [N][K]
+ * (device, must not overlap W's buffers).  1 <= r <= QLORA_MAX_RANK;
+ * rows*cols*2, r*cols*2 and rows*r*2 below 2^31 (QL_ERR_SHAPE otherwise). */
+int qlora_merge(const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                uint16_t* W_out, void* stream);
+
+/* Take the adapter back out of a merged weight (swapping adapters on a
+ * merged model, IBM "What is LoRA?"):
+ *   W_out[n][k] = bf16_RNE( fl32(W_merged[n][k]) - s * sum_j B[n][j] A[j][k] ).
+ * After qlora_merge each element comes back to W' within one bf16 unit in the
+ * last place (two roundings).  W_merged, W_out bf16 [rows][cols] (device);
+ * W_out may equal W_merged (in place).  cols % 8 == 0. */
+int qlora_unmerge(const uint16_t* W_merged, int64_t rows, int64_t cols, const uint16_t* A,
+                  const uint16_t* B, int r, float alpha, uint16_t* W_out, void* stream);
+
 /* Benchmark timing hook.  When set, later calls ON THIS THREAD record
  * fwd_begin / fwd_end (hipEvent_t handles the caller created) on the call's
  * stream immediately before and after the launch of the forward's main GEMM

@@ -144,3 +144,19 @@ def test_error_message_is_cleared_by_success():
     assert L.qlora_last_error() != b""
     assert L.nf4_storage_bytes(64, 64, 64, 256, None, None, None) == 0
     assert L.qlora_last_error() == b""
+
+
+def test_merge_rejects_bad_arguments():
+    L = q.lib()
+    w = _weight()
+    assert L.qlora_merge(None, FAKE, FAKE, 8, 16.0, FAKE, None) == -1
+    assert L.qlora_merge(ctypes.byref(w), None, FAKE, 8, 16.0, FAKE, None) == -1
+    assert L.qlora_merge(ctypes.byref(w), FAKE, FAKE, 0, 16.0, FAKE, None) == -3
+    assert L.qlora_merge(ctypes.byref(w), FAKE, FAKE, 129, 16.0, FAKE, None) == -3
+    assert L.qlora_merge(ctypes.byref(w), FAKE + 2, FAKE, 8, 16.0, FAKE, None) == -4
+    assert L.qlora_unmerge(FAKE, 0, 256, FAKE, FAKE, 8, 16.0, FAKE, None) == -2
+    assert L.qlora_unmerge(FAKE, 16, 12, FAKE, FAKE, 8, 16.0, FAKE, None) == -2
+    assert L.qlora_unmerge(FAKE, 16, 64, FAKE, FAKE, 200, 16.0, FAKE, None) == -3
+    assert L.qlora_unmerge(None, 16, 64, FAKE, FAKE, 8, 16.0, FAKE, None) == -1
+    assert L.qlora_unmerge(FAKE, 16, 64, FAKE, FAKE, 8, 16.0, FAKE + 8, None) == -4
+    assert L.qlora_unmerge(FAKE, 1 << 20, 1 << 12, FAKE, FAKE, 8, 16.0, FAKE, None) == -2
