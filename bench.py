@@ -223,6 +223,41 @@ def bench_decode(hip, reps=60):
     return out
 
 
+def bench_merge(hip, lay, reps=10):
+    """Adapter merge into a bf16 weight and its inverse, on the up projection
+    (28672x8192, r=64).  Algorithmic bytes: merge reads the NF4 weight
+    (0.516 B/weight) and the adapters and writes bf16 (2 B/weight); unmerge
+    reads and writes bf16."""
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    st = torch.cuda.current_stream().cuda_stream
+    out = torch.empty(lay.N, lay.K, dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out)
+    nk = lay.N * lay.K
+    adapters = 2 * lay.r * (lay.N + lay.K)
+    res = {}
+    for name, fn, nbytes in (
+            ("merge", lambda: q.qlora_merge(lay.w, lay.A, lay.B, lay.alpha, out=out),
+             nk * (0.5 + 1 / 64 + 4 / 16384 + 2) + adapters),
+            ("unmerge", lambda: q.qlora_unmerge(out, lay.A, lay.B, lay.alpha, out=out2),
+             nk * 4 + adapters)):
+        for _ in range(3):
+            fn()
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for _ in range(reps):
+            fn()
+        hip.record(e1, st)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"W": f"{lay.N}x{lay.K}", "r": lay.r, "us_per_call": round(ms * 1e3, 1),
+                     "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del out, out2
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_library_reference(hip, layers, reps=10):
     """Context only, not part of the path: a dense bf16 matmul from the vendor
     library (torch -> hipBLASLt) on the same shapes as the two fused forward
@@ -426,6 +461,8 @@ def main():
         extras["decode"] = bench_decode(hip)
 
     if not args.no_extras:
+        log("[bench] adapter merge")
+        extras["merge"] = bench_merge(hip, up)
         log("[bench] library reference")
         extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
 
