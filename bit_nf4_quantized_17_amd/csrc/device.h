@@ -64,6 +64,7 @@ __device__ __forceinline__ float dpp_f32(float x) {
 }
 constexpr int DPP_QUAD_XOR1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 
 // max over each aligned group of 8 lanes
@@ -72,6 +73,12 @@ __device__ __forceinline__ float max8(float x) {
   x = fmaxf(x, dpp_f32<DPP_QUAD_XOR2>(x));
   x = fmaxf(x, dpp_f32<DPP_ROW_HALF_MIRROR>(x));
   return x;
+}
+
+// max over each aligned group of 16 lanes (one DPP row)
+__device__ __forceinline__ float max16(float x) {
+  x = max8(x);
+  return fmaxf(x, dpp_f32<DPP_ROW_MIRROR>(x));
 }
 
 // max over the whole wave (result valid in every lane)

@@ -43,18 +43,22 @@ const EncodeCuts& encode_cuts() {
 
 // ---------------------------------------------------------------------------
 // Quantize.  One workgroup (256 threads) per group of 256 blocks (16384
-// contiguous fp32, 64 KiB).  A wave pass covers 8 consecutive blocks: 8 lanes
-// per block, 8 consecutive elements per lane (two 16-byte loads), so each
-// lane emits one 32-bit word of packed codes.
+// contiguous fp32, 64 KiB).  Each wave load instruction reads 1 KiB of
+// contiguous weights: four blocks, 16 lanes per block, 4 elements per lane;
+// each wave reads its own contiguous quarter of the group, and a lane issues
+// all 16 of its loads before any arithmetic.  The packed codes
+// (two bytes per lane and load) and the group's 8-bit scales are collected in
+// LDS and leave as 16-byte nontemporal stores, which costs HBM less than
+// narrow stores interleaved with the read stream.
 //
 // Exact encode without a per-element division: with y = RN(1/a) the product
 // q = RN(x*y) lies within 2 ulp of RN(x/a).  The code of v is the number of
-// decision points cut[j] <= v; a 256-bin LDS table over [-1, 1] holds, per
-// bin, the only decision point that can fall inside it (bins are 1/128 wide,
-// decision points >= 0.079 apart) and the count below it.  Whenever q is
-// within 2^-20 of that decision point, or the block scale is outside
-// [2^-100, 2^100] (including an all-zero block), the lane redoes the element
-// with an IEEE division, so the result always equals code(RN(x/a)).
+// decision points cut[j] <= v; an LDS table of 1/128-wide bins over [-1, 1]
+// holds, per bin, the only decision point that can fall inside it (decision
+// points are >= 0.079 apart) and the count below it.  Whenever q is within
+// 2^-20 of that decision point, or the block scale is outside [2^-100, 2^100]
+// (including an all-zero block), the lane redoes its elements with an IEEE
+// division, so the result always equals code(RN(x/a)).
 // ---------------------------------------------------------------------------
 constexpr int QBINS = 256;
 constexpr float BIN_PAD = 0x1p-12f;
@@ -65,6 +69,7 @@ struct BinEntry {
   int base;    // number of decision points below the padded bin
 };
 
+// clamped bin of a value in [-1, 1] (slow path)
 __device__ __forceinline__ int bin_of(float q) {
   int b = (int)((q + 1.0f) * 128.0f);
   return min(max(b, 0), QBINS - 1);
@@ -76,7 +81,10 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                                   float* __restrict__ dscale,
                                                   float* __restrict__ absmax_out,
                                                   EncodeCuts cuts) {
-  __shared__ BinEntry s_bin[QBINS];
+  // entry QBINS repeats entry QBINS - 1, for q a hair above 1 on the fast path
+  __shared__ BinEntry s_bin[QBINS + 1];
+  __shared__ uint16_t s_codes[256 * 16];  // the group's packed codes, 32 bytes per block
+  __shared__ uint32_t s_q[64];            // the group's 8-bit scales
   __shared__ float s_amax[256];
   __shared__ float s_wmax[4];
 
@@ -85,29 +93,30 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int64_t b0 = g * 256;
   const int nbg = (int)min<int64_t>(256, nblocks - b0);
 
-  // issue all loads first, then build the bin table while they are in flight
-  f32x4_t v[8][2];
+  // wave w streams its own 16 KiB: load p covers blocks 4 (16w + p) .. 4 (16w + p) + 3
+  f32x4_t v[16];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    int bi = p * 32 + wave * 8 + (lane >> 3);
+  for (int p = 0; p < 16; ++p) {
+    const int bi = (wave * 16 + p) * 4 + (lane >> 4);
     if (bi < nbg) {
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(W + (b0 + bi) * 64 + (lane & 7) * 8);
-      v[p][0] = __builtin_nontemporal_load(src);
-      v[p][1] = __builtin_nontemporal_load(src + 1);
+      v[p] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t*>(W + (b0 + bi) * 64 + (lane & 15) * 4));
     } else {
-      v[p][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      v[p][1] = v[p][0];
+      v[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
-  for (int i = tid; i < QBINS; i += 256) {
-    float lo = -1.0f + (float)i * (1.0f / 128.0f) - BIN_PAD;
-    float hi = -1.0f + (float)(i + 1) * (1.0f / 128.0f) + BIN_PAD;
+  // bin table, built while the loads are in flight
+  for (int i = tid; i <= QBINS; i += 256) {
+    const int ib = min(i, QBINS - 1);
+    const float lo = -1.0f + (float)ib * (1.0f / 128.0f) - BIN_PAD;
+    const float hi = -1.0f + (float)(ib + 1) * (1.0f / 128.0f) + BIN_PAD;
     int base = 0;
     float cut = 4.0f;
+#pragma unroll
     for (int j = 0; j < 15; ++j) {
-      float c = cuts.cut[j];
-      if (c < lo) base++;
-      else if (c <= hi) cut = c;
+      const float c = cuts.cut[j];
+      base += (c < lo) ? 1 : 0;
+      cut = (c >= lo && c <= hi) ? c : cut;
     }
     s_bin[i].cut = cut;
     s_bin[i].base = base;
@@ -116,48 +125,51 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   __syncthreads();  // bin table ready
 
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    int bi = p * 32 + wave * 8 + (lane >> 3);
-    float x[8] = {v[p][0].x, v[p][0].y, v[p][0].z, v[p][0].w,
-                  v[p][1].x, v[p][1].y, v[p][1].z, v[p][1].w};
-    float m = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-    const float a = max8(m);
+  for (int p = 0; p < 16; ++p) {
+    const int bi = (wave * 16 + p) * 4 + (lane >> 4);
+    const float x[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+    const float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    const float a = max16(m);
     const bool safe = (a >= 0x1p-100f) && (a <= 0x1p100f);
-    const float y = 1.0f / a;  // correctly rounded (IEEE division)
+    // correctly rounded reciprocal; 0 for an unsafe scale keeps the fast
+    // path's bin index in range (that lane takes the slow path anyway)
+    const float y = safe ? 1.0f / a : 0.0f;
     uint32_t word = 0;
     bool near = !safe;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float q = x[e] * y;
-      BinEntry be = s_bin[bin_of(q)];
-      int c = be.base + (q >= be.cut ? 1 : 0);
-      near |= fabsf(q - be.cut) <= NEAR_EPS;
-      word |= (uint32_t)c << (4 * e);
+    for (int e = 0; e < 4; ++e) {
+      const float q = x[e] * y;
+      // |q| <= 1 + 2^-23, so fma(q, 128, 128) = RN(q + 1) * 128 truncates to
+      // 0 .. 256 with no clamp
+      const BinEntry be = s_bin[(int)__builtin_fmaf(q, 128.0f, 128.0f)];
+      const float dlt = q - be.cut;  // zero only when q == cut (denormals kept)
+      word |= (uint32_t)(be.base + (dlt >= 0.0f ? 1 : 0)) << (4 * e);
+      near |= fabsf(dlt) <= NEAR_EPS;
     }
-    if (near) {  // rare: exact quotients for this lane's 8 elements
+    if (near) {  // rare: exact quotients for this lane's 4 elements
       word = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4; ++e) {
         int c = 7;  // all-zero block: the exact zero level
         if (a > 0.0f) {
-          float q = x[e] / a;
-          BinEntry be = s_bin[bin_of(q)];
+          const float q = x[e] / a;
+          const BinEntry be = s_bin[bin_of(q)];
           c = be.base + (q >= be.cut ? 1 : 0);
         }
         word |= (uint32_t)c << (4 * e);
       }
     }
-    if (bi < nbg) {
-      __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(codes + (b0 + bi) * 32 + (lane & 7) * 4));
-      if ((lane & 7) == 0) {
-        s_amax[bi] = a;
-        if (absmax_out) absmax_out[b0 + bi] = a;
-      }
+    s_codes[bi * 16 + (lane & 15)] = (uint16_t)word;  // even element in the low nibble
+    if (bi < nbg && (lane & 15) == 0) {
+      s_amax[bi] = a;
+      if (absmax_out) absmax_out[b0 + bi] = a;
     }
   }
   __syncthreads();
+
+  for (int i = tid; i < nbg * 2; i += 256)
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&s_codes[i * 8]),
+                                reinterpret_cast<u32x4_t*>(codes + b0 * 32) + i);
 
   // double quantization of this group's block scales
   const float a_t = tid < nbg ? s_amax[tid] : 0.0f;
@@ -167,7 +179,15 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const float c = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
   const float d = c / 448.0f;
   if (tid == 0) dscale[g] = d;
-  if (tid < nbg) qscale[b0 + tid] = (uint8_t)(d == 0.0f ? 0u : e4m3_encode(a_t / d));
+  reinterpret_cast<uint8_t*>(s_q)[tid] = (uint8_t)(d == 0.0f ? 0u : e4m3_encode(a_t / d));
+  __syncthreads();
+  if (nbg == 256) {
+    if (tid < 16)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&s_q[tid * 4]),
+                                  reinterpret_cast<u32x4_t*>(qscale + b0) + tid);
+  } else if (tid < nbg) {
+    qscale[b0 + tid] = reinterpret_cast<const uint8_t*>(s_q)[tid];
+  }
 }
 
 hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
