@@ -223,11 +223,12 @@ def bench_decode(hip, reps=60):
     return out
 
 
-def bench_merge(hip, lay, reps=10):
-    """Adapter merge into a bf16 weight and its inverse, on the up projection
-    (28672x8192, r=64).  Algorithmic bytes: merge reads the NF4 weight
-    (0.516 B/weight) and the adapters and writes bf16 (2 B/weight); unmerge
-    reads and writes bf16."""
+def bench_bf16_weight(hip, lay, reps=10):
+    """The calls that write a bf16 weight, on the up projection (28672x8192,
+    r=64): nf4_dequantize, the adapter merge and its inverse.  Algorithmic
+    bytes: dequantize reads the NF4 weight (0.516 B/weight) and writes bf16
+    (2 B/weight); merge also reads the adapters; unmerge reads and writes
+    bf16.  The 470 MB output alone exceeds the 256 MB Infinity Cache."""
     import torch
     import bit_nf4_quantized_17_amd as q
     st = torch.cuda.current_stream().cuda_stream
@@ -237,6 +238,7 @@ def bench_merge(hip, lay, reps=10):
     adapters = 2 * lay.r * (lay.N + lay.K)
     res = {}
     for name, fn, nbytes in (
+            ("dequantize", lambda: q.nf4_dequantize(lay.w, out=out), nk * (0.5 + 1 / 64 + 4 / 16384 + 2)),
             ("merge", lambda: q.qlora_merge(lay.w, lay.A, lay.B, lay.alpha, out=out),
              nk * (0.5 + 1 / 64 + 4 / 16384 + 2) + adapters),
             ("unmerge", lambda: q.qlora_unmerge(out, lay.A, lay.B, lay.alpha, out=out2),
@@ -251,8 +253,10 @@ def bench_merge(hip, lay, reps=10):
         hip.record(e1, st)
         ms = hip.elapsed_ms(e0, e1) / reps
         gbs = nbytes / (ms * 1e-3) / 1e9
-        res[name] = {"W": f"{lay.N}x{lay.K}", "r": lay.r, "us_per_call": round(ms * 1e3, 1),
+        res[name] = {"W": f"{lay.N}x{lay.K}", "us_per_call": round(ms * 1e3, 1),
                      "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        if name != "dequantize":
+            res[name]["r"] = lay.r
     del out, out2
     torch.cuda.empty_cache()
     return res
@@ -461,8 +465,10 @@ def main():
         extras["decode"] = bench_decode(hip)
 
     if not args.no_extras:
-        log("[bench] adapter merge")
-        extras["merge"] = bench_merge(hip, up)
+        log("[bench] dequantize, adapter merge")
+        bw = bench_bf16_weight(hip, up)
+        extras["dequantize"] = bw.pop("dequantize")
+        extras["merge"] = bw
         log("[bench] library reference")
         extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
 

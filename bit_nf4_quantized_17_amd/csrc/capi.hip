@@ -166,6 +166,7 @@ int nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, void* stream) {
   int rc = check_weight(w);
   if (rc) return rc;
   if (!W_bf16) return fail(QL_ERR_NULL, "output is NULL");
+  if ((w->rows * w->cols / 64 + 255) / 256 > 0x7fffffffLL) return fail(QL_ERR_SHAPE, "weight too large");
   if (!aligned16(W_bf16)) return fail(QL_ERR_ALIGN, "output must be 16-byte aligned");
   return hip_status(launch_dequantize(view(w), W_bf16, (hipStream_t)stream), "nf4_dequantize launch");
 }

@@ -200,40 +200,63 @@ hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: w' = bf16_RNE(fl32(L[code] * fl32(E4M3(q) * d))).  Each thread
-// converts 16 consecutive elements (8 code bytes -> 32 output bytes); the
-// level table sits in LDS.
+// Dequantize: w' = bf16_RNE(fl32(L[code] * fl32(E4M3(q) * d))).  One
+// workgroup (4 waves) per group of 256 blocks, so d is one scalar load; wave w
+// writes its own contiguous 64 blocks (8 KiB of bf16).  In step j a lane takes
+// 8 codes of block 8j + lane/8 (one 4-byte load) and writes their 8 bf16 values
+// with one 16-byte store, so every load instruction reads 256 contiguous bytes
+// and every store instruction writes 1 KiB.  All loads are issued before any
+// arithmetic; the level table sits in LDS.
 // ---------------------------------------------------------------------------
+constexpr int DQ_STEPS = 8;  // 8 blocks per wave and step
+
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ qscale,
                                                     const float* __restrict__ dscale,
-                                                    int64_t nchunks, u16* __restrict__ out) {
+                                                    int64_t nblocks, u16* __restrict__ out) {
   __shared__ float s_L[16];
-  if (threadIdx.x < 16) s_L[threadIdx.x] = __uint_as_float(kNF4LevelBits[threadIdx.x]);
-  __syncthreads();
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < nchunks; ch += stride) {
-    const int64_t blk = ch >> 2;  // 4 chunks of 16 per block of 64
-    const float sc = e4m3_decode(qscale[blk]) * dscale[blk >> 8];
-    const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(codes) + ch);
-    uint32_t o[8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t g = blockIdx.x;
+  const int64_t b0 = g * 256 + wave * 64;               // first block of this wave
+  const int64_t nbw = min<int64_t>(64, nblocks - b0);  // its blocks (<= 0 past the end)
+  if (tid < 16) s_L[tid] = __uint_as_float(kNF4LevelBits[tid]);
+  const float d = dscale[g];
+  uint32_t c[DQ_STEPS], qv[DQ_STEPS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t byte = ((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu;
+  for (int j = 0; j < DQ_STEPS; ++j) {
+    const int blk = j * 8 + (lane >> 3);
+    if (blk < nbw) {
+      c[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + (b0 + blk) * 32) +
+                                        (lane & 7));
+      qv[j] = qscale[b0 + blk];
+    } else {
+      c[j] = 0;
+      qv[j] = 0;
+    }
+  }
+  __syncthreads();  // level table ready
+#pragma unroll
+  for (int j = 0; j < DQ_STEPS; ++j) {
+    const int blk = j * 8 + (lane >> 3);
+    const float sc = e4m3_decode(qv[j]) * d;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t byte = (c[j] >> (8 * i)) & 0xFFu;  // even element in the low nibble
       o[i] = pack_bf16x2(s_L[byte & 15u] * sc, s_L[byte >> 4] * sc);
     }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + ch * 16);
-    __builtin_nontemporal_store(u32x4_t{o[0], o[1], o[2], o[3]}, dst);
-    __builtin_nontemporal_store(u32x4_t{o[4], o[5], o[6], o[7]}, dst + 1);
+    if (blk < nbw)
+      __builtin_nontemporal_store(u32x4_t{o[0], o[1], o[2], o[3]},
+                                  reinterpret_cast<u32x4_t*>(out + (b0 + blk) * 64 + (lane & 7) * 8));
   }
 }
 
 hipError_t launch_dequantize(const NF4View& w, u16* out, hipStream_t s) {
-  const int64_t nchunks = w.N * w.K / 16;
-  int64_t grid = (nchunks + 255) / 256;
-  grid = std::min<int64_t>(grid, 256 * 64);
-  hipLaunchKernelGGL(k_dequantize, dim3((unsigned)grid), dim3(256), 0, s, w.codes, w.qscale,
-                     w.dscale, nchunks, out);
+  const int64_t nb = w.N * w.K / 64;
+  const int64_t ng = (nb + 255) / 256;
+  hipLaunchKernelGGL(k_dequantize, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
+                     w.dscale, nb, out);
   return hipGetLastError();
 }
 
