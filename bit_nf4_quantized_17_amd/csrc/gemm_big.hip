@@ -48,8 +48,15 @@ enum { MODE_FWD = 0, MODE_DX = 1 };
 
 template <int MODE>
 constexpr int b_elems() { return MODE == MODE_FWD ? BF_ELEMS : BT_ELEMS; }
+// epilogue staging: each wave's 128 x 64 bf16 block, rows padded to 72
+constexpr int EPITCH = 72;
+constexpr int E_ELEMS = 128 * EPITCH;
 template <int MODE>
-constexpr size_t lds_bytes() { return (size_t)2 * (A_ELEMS + b_elems<MODE>()) * 2; }
+constexpr size_t lds_bytes() {
+  const size_t main = (size_t)2 * (A_ELEMS + b_elems<MODE>()) * 2;
+  const size_t epi = (size_t)(NTHREADS / 64) * E_ELEMS * 2;
+  return main > epi ? main : epi;
+}
 
 struct BigArgs {
   const u16* a; int64_t lda; bool a_vec;   // X [M][K] or dY [M][N]
@@ -58,7 +65,7 @@ struct BigArgs {
   const float* la;                         // T or U, fp32 [M][r]
   const u16* lb;                           // B [N][r] (forward) or A [r][K] (backward)
   int r; float s; bool la_vec; bool lb_vec;
-  u16* out; int64_t ldo;
+  u16* out; int64_t ldo; bool out_vec;   // out_vec: 16-byte aligned rows
 };
 
 typedef __attribute__((address_space(3))) short lds_short;
@@ -453,17 +460,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   }
 
   // ---- epilogue ----
+  // Each wave rounds its 128 x 64 block to bf16 into its own LDS region
+  // (lanes l and l^1 hold neighbouring columns of the same rows, so one DPP
+  // swap per pair of values gives each lane a packed pair), then writes it
+  // back out as 16-byte row segments: 8 lanes cover one 128-byte row.  The
+  // main loop's last barrier has freed LDS; the regions are disjoint, and a
+  // wave's LDS operations complete in order, so no barrier is needed.
+  u16* sE = smem + wave * E_ELEMS;
+  const bool odd = lane & 1;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t j = j0 + wn * 64 + b * 32 + (lane & 31);
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t i = m0 + wm * 128 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (i < p.M && j < p.J) p.out[i * p.ldo + j] = f32_to_bf16(acc[a][b][v]);
+      for (int v = 0; v < 16; v += 2) {
+        const float x0 = acc[a][b][v], x1 = acc[a][b][v + 1];
+        const float got = dpp_f32<DPP_QUAD_XOR1>(odd ? x0 : x1);
+        const int row = a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3) + (odd ? 1 : 0);
+        const int col = b * 32 + ((lane & 31) & ~1);
+        *reinterpret_cast<uint32_t*>(sE + row * EPITCH + col) =
+            odd ? pack_bf16x2(got, x1) : pack_bf16x2(x0, got);
+      }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = q * 8 + (lane >> 3), col = (lane & 7) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(sE + row * EPITCH + col);
+    const int64_t i = m0 + wm * 128 + row, j = j0 + wn * 64 + col;
+    if (i < p.M) {
+      u16* dst = p.out + i * p.ldo + j;
+      if (p.out_vec && j + 8 <= p.J) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (j + e < p.J) dst[e] = (u16)(w4[e >> 1] >> (16 * (e & 1)));
       }
     }
+  }
 }
 
 static bool vec_ok(const void* ptr, int64_t ld) {
@@ -506,7 +540,7 @@ hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const floa
   p.M = M; p.J = w.N; p.C = w.K;
   p.la = T; p.lb = B; p.r = r; p.s = s;
   p.la_vec = big::vec_ok(T, r * 2); p.lb_vec = big::vec_ok(B, r);
-  p.out = Y; p.ldo = w.N;
+  p.out = Y; p.ldo = w.N; p.out_vec = big::vec_ok(Y, w.N);
   return big::launch<big::MODE_FWD>(p, st);
 }
 
@@ -520,7 +554,7 @@ hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const floa
   p.M = M; p.J = w.K; p.C = w.N;
   p.la = U; p.lb = A; p.r = r; p.s = s;
   p.la_vec = big::vec_ok(U, r * 2); p.lb_vec = big::vec_ok(A, w.K);
-  p.out = dX; p.ldo = w.K;
+  p.out = dX; p.ldo = w.K; p.out_vec = big::vec_ok(dX, w.K);
   return big::launch<big::MODE_DX>(p, st);
 }
 
