@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_bf16_rne_double.restype = ctypes.c_uint16
         L.oracle_lora_merge.argtypes = [P, I64, I64, P, P, I, D, I, P, I]
         L.oracle_lora_merge.restype = I
+        L.oracle_swiglu.argtypes = [P, P, I64, P]
+        L.oracle_swiglu.restype = None
         _lib = L
     return _lib
 
@@ -251,3 +253,14 @@ def lora_merge(W_base, A, B, alpha: float, sign: int = 1, threads: int | None = 
     _check(lib().oracle_lora_merge(_ptr(Wb), N, K, _ptr(Ab), _ptr(Bb), r, float(alpha), int(sign), _ptr(out),
                                    threads or default_threads()), "lora_merge")
     return out
+
+
+def swiglu(G, U):
+    """H = silu(G) * U elementwise in double, silu(x) = x / (1 + e^-x): the gated
+    activation of a Llama-style MLP applied to its gate and up projections."""
+    g = np.ascontiguousarray(G, dtype=np.float64)
+    u = np.ascontiguousarray(U, dtype=np.float64)
+    assert g.shape == u.shape
+    h = np.empty_like(g)
+    lib().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h

@@ -574,3 +574,13 @@ int oracle_lora_merge(const uint16_t* W_base, int64_t N, int64_t K, const uint16
   parallel_for(N, nthreads, merge_range, &c);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Gated activation of the gate and up projections: H = silu(G) * U.        */
+/* ------------------------------------------------------------------------ */
+void oracle_swiglu(const double* G, const double* U, int64_t n, double* H) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double g = G[i];
+    H[i] = g / (1.0 + exp(-g)) * U[i];
+  }
+}

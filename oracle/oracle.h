@@ -127,6 +127,14 @@ int oracle_lora_merge(const uint16_t* W_base, int64_t N, int64_t K, const uint16
                       const uint16_t* B, int r, double alpha, int sign, uint16_t* W_out,
                       int nthreads);
 
+/* The gated activation of a Llama-style MLP, whose gate and up projections
+ * both read the same input (the Transformers "Bitsandbytes" and Ultralytics
+ * "QLoRA" pages fine-tune Llama-2 models):
+ *   H[i] = silu(G[i]) * U[i],  silu(x) = x / (1 + e^-x)
+ * in double, elementwise over n values.  G and U are the two projections'
+ * outputs (each a qlora forward); H may equal G or U. */
+void oracle_swiglu(const double* G, const double* U, int64_t n, double* H);
+
 #ifdef __cplusplus
 }
 #endif

@@ -507,3 +507,25 @@ def test_merge_is_exact_on_small_integers(orc):
     assert np.array_equal(got, bits(exact))
     back = orc.lora_merge(got, bits(Ai), bits(Bi), alpha, sign=-1)
     assert np.array_equal(back, bits(Wi))
+
+
+def test_swiglu_closed_forms(orc):
+    """silu(x) = x sigmoid(x) against forms the oracle does not use: the tanh
+    form (x/2)(1 + tanh(x/2)) for x >= 0, x e^x / (1 + e^x) for x < 0 (each
+    free of cancellation on its side), the odd part silu(x) - silu(-x) = x,
+    zero at zero, the identity for large x, and linearity in the up input."""
+    rng = np.random.default_rng(8)
+    g = np.concatenate([rng.normal(0.0, 3.0, 2000), [0.0, 1e-300, -1e-300, 2.0, -2.0, -30.0]])
+    one = np.ones_like(g)
+    h = orc.swiglu(g, one)
+    pos = g >= 0
+    tanh_form = 0.5 * g[pos] * (1.0 + np.tanh(0.5 * g[pos]))
+    assert np.allclose(h[pos], tanh_form, rtol=1e-14, atol=1e-300)
+    e = np.exp(g[~pos])
+    assert np.allclose(h[~pos], g[~pos] * e / (1.0 + e), rtol=1e-14, atol=1e-300)
+    assert np.allclose(h - orc.swiglu(-g, one), g, rtol=1e-13, atol=1e-15)
+    assert orc.swiglu(np.array([0.0]), np.array([5.0]))[0] == 0.0
+    assert orc.swiglu(np.array([2.0]), np.array([1.0]))[0] == pytest.approx(1.0 + math.tanh(1.0), rel=1e-15)
+    assert orc.swiglu(np.array([50.0]), np.array([1.0]))[0] == pytest.approx(50.0, rel=1e-15)
+    u = rng.normal(size=g.shape)
+    assert np.allclose(orc.swiglu(g, 3.0 * u), 3.0 * orc.swiglu(g, u), rtol=1e-14, atol=1e-300)
