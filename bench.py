@@ -262,6 +262,48 @@ def bench_bf16_weight(hip, lay, reps=10):
     return res
 
 
+def bench_dual(hip, lay, reps=10):
+    """Gate and up projections of one X (qlora_dual_fwd, both epilogues)
+    against two qlora_linear_fwd calls: two 28672x8192 NF4 weights, 4096
+    tokens, r=64.  The up layer is the step's up projection; the gate weight
+    and adapters are seeded synthetic tensors of the same shapes."""
+    import math
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    st = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20240)
+    Wg = torch.randn(lay.N, lay.K, generator=gen, device="cuda") * 0.02
+    wg = q.nf4_quantize(Wg)
+    del Wg
+    Ag = (torch.randn(lay.r, lay.K, generator=gen, device="cuda") / math.sqrt(lay.r)).to(torch.bfloat16)
+    Bg = (torch.randn(lay.N, lay.r, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    Yg = torch.empty_like(lay.Y)
+    Tg = torch.empty_like(lay.T)
+    fwd, _ = linear_flops(lay.M, lay.N, lay.K, lay.r)
+    res = {"W": f"2x {lay.N}x{lay.K}", "M": lay.M, "r": lay.r}
+    for name, fn in (
+            ("two_single_fwd", lambda: (q.qlora_linear_fwd(wg, lay.X, Ag, Bg, lay.alpha, Y=Yg, T=Tg,
+                                                           workspace=lay.wsf), lay.fwd())),
+            ("dual_separate", lambda: q.qlora_dual_fwd(wg, lay.w, lay.X, Ag, Bg, lay.A, lay.B, lay.alpha,
+                                                       workspace=lay.wsf)),
+            ("dual_swiglu", lambda: q.qlora_dual_fwd(wg, lay.w, lay.X, Ag, Bg, lay.A, lay.B, lay.alpha,
+                                                     swiglu=True, workspace=lay.wsf))):
+        for _ in range(2):
+            fn()
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for _ in range(reps):
+            fn()
+        hip.record(e1, st)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        res[name] = {"ms": round(ms, 4), "TFLOP/s": round(2 * fwd / (ms * 1e-3) / 1e12, 1)}
+    del wg, Ag, Bg, Yg, Tg
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_library_reference(hip, layers, reps=10):
     """Context only, not part of the path: a dense bf16 matmul from the vendor
     library (torch -> hipBLASLt) on the same shapes as the two fused forward
@@ -469,6 +511,8 @@ def main():
         bw = bench_bf16_weight(hip, up)
         extras["dequantize"] = bw.pop("dequantize")
         extras["merge"] = bw
+        log("[bench] gate/up dual projection")
+        extras["dual"] = bench_dual(hip, up)
         log("[bench] library reference")
         extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
 

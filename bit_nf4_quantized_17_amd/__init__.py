@@ -21,6 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
 
 QL_DTYPE_BF16 = 1
+QL_DUAL_SEPARATE = 1
+QL_DUAL_SWIGLU = 2
 QLORA_MAX_RANK = 128
 _STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_UNSUPPORTED",
            -4: "QL_ERR_ALIGN", -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
@@ -63,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_fwd_workspace_bytes.restype = SZ
     L.qlora_linear_fwd.argtypes = [WP, P, I64, P, P, I, F, I, P, P, P, SZ, P]
     L.qlora_linear_fwd.restype = I
+    L.qlora_dual_fwd.argtypes = [WP, WP, P, I64, P, P, P, P, I, F, I, I, P, P, P, P, P, P, SZ, P]
+    L.qlora_dual_fwd.restype = I
     L.qlora_bwd_workspace_bytes.argtypes = [I64, I64, I64, I]
     L.qlora_bwd_workspace_bytes.restype = SZ
     L.qlora_linear_bwd.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P, SZ, P]
@@ -238,6 +242,41 @@ def qlora_linear_fwd(w: NF4Weight, X, A, B, alpha: float, Y=None, T=None, worksp
                                   float(alpha), QL_DTYPE_BF16, Y.data_ptr(), T.data_ptr(), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))
     return Y, T
+
+
+def qlora_dual_fwd(w_gate: NF4Weight, w_up: NF4Weight, X, A_gate, B_gate, A_up, B_up,
+                   alpha: float, swiglu: bool = False, workspace=None, stream=None):
+    """Gate and up projections of one X in one kernel.  Returns
+    (Y_gate, Y_up, T_gate, T_up), or with swiglu=True (H, T_gate, T_up) where
+    H = bf16(silu(G) * U) from the fp32 sums."""
+    import torch
+    M, K = X.shape
+    r = A_gate.shape[0]
+    N = w_gate.rows
+    _need(X, torch.bfloat16, (M, w_gate.cols), "X")
+    for t, nm in ((A_gate, "A_gate"), (A_up, "A_up")):
+        _need(t, torch.bfloat16, (r, K), nm)
+    for t, nm in ((B_gate, "B_gate"), (B_up, "B_up")):
+        _need(t, torch.bfloat16, (N, r), nm)
+    dev = X.device
+    Tg = torch.empty(M, r, dtype=torch.float32, device=dev)
+    Tu = torch.empty(M, r, dtype=torch.float32, device=dev)
+    if swiglu:
+        H = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        Yg = Yu = None
+    else:
+        Yg = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        Yu = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        H = None
+    ws = _workspace(qlora_fwd_workspace_bytes(M, N, K, r), dev, workspace)
+    dg, du = w_gate.descriptor(), w_up.descriptor()
+    _check(lib().qlora_dual_fwd(ctypes.byref(dg), ctypes.byref(du), X.data_ptr(), M,
+                                A_gate.data_ptr(), B_gate.data_ptr(), A_up.data_ptr(), B_up.data_ptr(),
+                                r, float(alpha), QL_DTYPE_BF16,
+                                QL_DUAL_SWIGLU if swiglu else QL_DUAL_SEPARATE,
+                                _ptr(Yg), _ptr(Yu), _ptr(H), Tg.data_ptr(), Tu.data_ptr(), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)))
+    return (H, Tg, Tu) if swiglu else (Yg, Yu, Tg, Tu)
 
 
 def qlora_linear_bwd(w: NF4Weight, X, dY, A, B, alpha: float, T=None, want_dX: bool = True,

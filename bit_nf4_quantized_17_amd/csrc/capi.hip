@@ -231,6 +231,48 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   return hip_status(e, "qlora_linear_fwd: main launch");
 }
 
+int qlora_dual_fwd(const qlora_nf4_weight* w_gate, const qlora_nf4_weight* w_up, const uint16_t* X,
+                   int64_t M, const uint16_t* A_gate, const uint16_t* B_gate, const uint16_t* A_up,
+                   const uint16_t* B_up, int r, float alpha, int compute_dtype, int epilogue,
+                   uint16_t* Y_gate, uint16_t* Y_up, uint16_t* H, float* T_gate_save,
+                   float* T_up_save, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layer(w_gate, M, r, compute_dtype);
+  if (rc) return rc;
+  rc = check_weight(w_up);
+  if (rc) return rc;
+  if (w_up->rows != w_gate->rows || w_up->cols != w_gate->cols)
+    return fail(QL_ERR_SHAPE, "gate %lld x %lld and up %lld x %lld weights differ in shape",
+                (long long)w_gate->rows, (long long)w_gate->cols, (long long)w_up->rows,
+                (long long)w_up->cols);
+  if (epilogue != QL_DUAL_SEPARATE && epilogue != QL_DUAL_SWIGLU)
+    return fail(QL_ERR_UNSUPPORTED, "epilogue=%d (QL_DUAL_SEPARATE or QL_DUAL_SWIGLU)", epilogue);
+  uint16_t* out1 = epilogue == QL_DUAL_SEPARATE ? Y_gate : H;
+  uint16_t* out2 = epilogue == QL_DUAL_SEPARATE ? Y_up : nullptr;
+  if (!X || !A_gate || !B_gate || !A_up || !B_up || !T_gate_save || !T_up_save || !out1 ||
+      (epilogue == QL_DUAL_SEPARATE && !out2))
+    return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(X) || !aligned16(A_gate) || !aligned16(B_gate) || !aligned16(A_up) ||
+      !aligned16(B_up) || !aligned16(T_gate_save) || !aligned16(T_up_save) || !aligned16(out1) ||
+      (out2 && !aligned16(out2)))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const int64_t N = w_gate->rows, K = w_gate->cols;
+  if ((N + 256) * K / 2 >= ((int64_t)1 << 31) || K * 2 * 512 >= ((int64_t)1 << 31))
+    return fail(QL_ERR_SHAPE, "weight too large for the dual kernel (32-bit offsets)");
+  const size_t need = align256((size_t)skinny_partial_elems(M, K, r) * sizeof(float));
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (workspace && !aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_lora_down(X, A_gate, M, K, r, (float*)workspace, T_gate_save, st);
+  if (e == hipSuccess) e = launch_lora_down(X, A_up, M, K, r, (float*)workspace, T_up_save, st);
+  if (e != hipSuccess) return hip_status(e, "qlora_dual_fwd: lora_down launch");
+  record(g_hook.fwd_begin, st);
+  e = launch_fwd_dual(view(w_gate), view(w_up), X, M, T_gate_save, T_up_save, B_gate, B_up, r,
+                      alpha / (float)r, epilogue == QL_DUAL_SEPARATE ? 1 : 2, out1, out2, st);
+  record(g_hook.fwd_end, st);
+  return hip_status(e, "qlora_dual_fwd: main launch");
+}
+
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QLORA_MAX_RANK) return 0;
   return bwd_layout(M, N, K, r).total;

@@ -70,6 +70,11 @@ hipError_t launch_lora_da(const float* U, const u16* X, int64_t M, int64_t K, in
 // Y = X W'^T + s T B^T
 hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const float* T,
                            const u16* B, int r, float s, u16* Y, hipStream_t st);
+// gate and up projections of one X: Yg = X Wg'^T + s Tg Bg^T, Yu likewise;
+// epilogue 1 writes both, 2 writes bf16(silu(g) * u) into Yg (Yu unused)
+hipError_t launch_fwd_dual(const NF4View& wg, const NF4View& wu, const u16* X, int64_t M,
+                           const float* Tg, const float* Tu, const u16* Bg, const u16* Bu, int r,
+                           float s, int epilogue, u16* Yg, u16* Yu, hipStream_t st);
 // dX = dY W' + s U A
 hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const float* U,
                           const u16* A, int r, float s, u16* dX, hipStream_t st);

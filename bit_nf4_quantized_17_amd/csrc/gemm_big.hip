@@ -27,7 +27,20 @@
 // The LoRA term is a prologue: the accumulators start as (s T) B^T or
 // (s U) A, with s T / s U rounded to bf16 on the way to LDS (rank r <= 128 in
 // steps of 64), then the base product accumulates on top.
+//
+// Dual projection (forward only): two weights of one shape that read the
+// same X, such as the gate and up projections of a Llama-style MLP (the
+// models the Transformers "Bitsandbytes" and Ultralytics pages fine-tune), in
+// one kernel.  A tile's 256 weight rows are 128 output columns of each
+// weight, interleaved in 32-row slices (gate n0..n0+31, up n0..n0+31, gate
+// n0+32.., ...), so each wave's two 32-column accumulator blocks hold the
+// gate and up sums of the same outputs, and the X tile is read once for both.
+// The two LoRA terms share one prologue of contraction 2r: the A side is
+// [T_gate | T_up] and a gate row of the B side is [B_gate[n] | 0], an up row
+// [0 | B_up[n]].  The epilogue writes both outputs, or silu(g) * u.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "device.h"
@@ -66,7 +79,16 @@ struct BigArgs {
   const u16* lb;                           // B [N][r] (forward) or A [r][K] (backward)
   int r; float s; bool la_vec; bool lb_vec;
   u16* out; int64_t ldo; bool out_vec;   // out_vec: 16-byte aligned rows
+  // dual projection only: the second weight, its T and B, its output
+  NF4View w2; const float* la2; const u16* lb2; u16* out2;
 };
+
+enum { DUAL_NONE = 0, DUAL_SEPARATE = 1, DUAL_SWIGLU = 2 };
+
+// dual projection: tile row t (0..255) holds output column n0 + dual_col(t)
+// of the gate weight (dual_src(t) == 0) or of the up weight (1)
+__device__ __forceinline__ int dual_col(int t) { return 32 * (t >> 6) + (t & 31); }
+__device__ __forceinline__ int dual_src(int t) { return (t >> 5) & 1; }
 
 typedef __attribute__((address_space(3))) short lds_short;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -202,6 +224,36 @@ __device__ __forceinline__ void lora_a_tile(const float* src, int64_t ld, int64_
   }
 }
 
+// Dual prologue, A side: columns c < r of the contraction come from T_gate,
+// columns r .. 2r - 1 from T_up (both fp32 [M][r]), times s, rounded to bf16.
+__device__ __forceinline__ void lora_a_tile_dual(const float* la, const float* la2, int r,
+                                                 int64_t rows, int64_t m0, int64_t c0, bool vec,
+                                                 float s, u16* sA, int tid) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t row = m0 + tid / 8 + 64 * q;
+    const int64_t c = c0 + (tid % 8) * 8;
+    float x[8];
+    if (vec && row < rows && c + 8 <= 2 * r) {  // r % 8 == 0: a chunk lies in one source
+      const float* src = c < r ? la + row * r + c : la2 + row * r + (c - r);
+      const float4 u = *reinterpret_cast<const float4*>(src);
+      const float4 v = *reinterpret_cast<const float4*>(src + 4);
+      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t ce = c + e;
+        x[e] = row >= rows || ce >= 2 * r ? 0.0f : ce < r ? la[row * r + ce] : la2[row * r + ce - r];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= s;
+    *reinterpret_cast<uint4*>(sA + (tid / 8 + 64 * q) * APITCH + (tid % 8) * 8) =
+        make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7]));
+  }
+}
+
 // where the thread's 32 dequantized values go: forward tile [256 n][FPITCH],
 // block row tid/2; backward tile [64 n][TPITCH], block (tid/2) = 4 per row
 template <int MODE>
@@ -248,6 +300,35 @@ __device__ __forceinline__ void lora_b_tile(const BigArgs& p, u16* sB, int64_t j
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (c + e < cols) v[e >> 1] |= (uint32_t)p.lb[row * ld + c + e] << (16 * (e & 1));
+    }
+    *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Dual prologue, B side, in the forward weight tile's layout: tile row t is
+// [B_gate[n] | 0] for a gate row and [0 | B_up[n]] for an up row, n = n0 +
+// dual_col(t); the thread fills row tid/2, columns c0 + 32*(tid%2) .. +32.
+__device__ __forceinline__ void lora_b_tile_dual(const BigArgs& p, u16* sB, int64_t n0, int64_t c0,
+                                                 int tid) {
+  u16* dst = sB + (tid >> 1) * FPITCH + 32 * (tid & 1);
+  const int t = tid >> 1, src = dual_src(t);
+  const int64_t n = n0 + dual_col(t);
+  const u16* lb = src ? p.lb2 : p.lb;
+  const int64_t lo = src ? p.r : 0;  // this row's nonzero contraction range: lo .. lo + r - 1
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t c = c0 + 32 * (tid & 1) + 8 * q;
+    uint32_t v[4] = {0, 0, 0, 0};
+    if (n < p.J) {
+      if (p.lb_vec && c >= lo && c + 8 <= lo + p.r) {
+        const uint4 u = *reinterpret_cast<const uint4*>(lb + n * p.r + (c - lo));
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c + e >= lo && c + e < lo + p.r)
+            v[e >> 1] |= (uint32_t)lb[n * p.r + (c + e - lo)] << (16 * (e & 1));
+      }
     }
     *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(v[0], v[1], v[2], v[3]);
   }
@@ -371,7 +452,7 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, int DUAL>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   extern __shared__ __attribute__((aligned(16))) u16 smem[];
   u16* sA[2] = {smem, smem + A_ELEMS};
@@ -380,7 +461,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int64_t j0 = (int64_t)blockIdx.y * BN;
+  // output column tile start (a dual tile covers BN / 2 columns of each weight)
+  const int64_t j0 = (int64_t)blockIdx.y * (DUAL ? BN / 2 : BN);
 
   f32x16_t acc[4][2];
 #pragma unroll
@@ -391,10 +473,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
   // ---- LoRA prologue: acc = sum_{c < r} bf16(s la(m, c)) lb(j, c) ----
-  for (int64_t c0 = 0; c0 < p.r; c0 += BK) {
+  for (int64_t c0 = 0; c0 < (DUAL ? 2 * p.r : p.r); c0 += BK) {
     __syncthreads();
-    lora_a_tile(p.la, p.r, p.M, p.r, m0, c0, p.la_vec, p.s, sA[0], tid);
-    lora_b_tile<MODE>(p, sB[0], j0, c0, tid);
+    if constexpr (DUAL) {
+      lora_a_tile_dual(p.la, p.la2, p.r, p.M, m0, c0, p.la_vec, p.s, sA[0], tid);
+      lora_b_tile_dual(p, sB[0], j0, c0, tid);
+    } else {
+      lora_a_tile(p.la, p.r, p.M, p.r, m0, c0, p.la_vec, p.s, sA[0], tid);
+      lora_b_tile<MODE>(p, sB[0], j0, c0, tid);
+    }
     __syncthreads();
     mma_stage<MODE>(acc, sA[0], sB[0], wm, wn, lane);
   }
@@ -407,9 +494,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   // of stages past the end read zeros or unused data and are never consumed.
   Bufs bf;
   bf.a = rsrc(p.a, (uint32_t)(p.M * p.lda * 2));
-  bf.codes = rsrc(p.w.codes, (uint32_t)(p.w.N * p.w.K / 2));
-  bf.qscale = rsrc(p.w.qscale, (uint32_t)(p.w.N * p.w.K / 64));
-  bf.dscale = rsrc(p.w.dscale, (uint32_t)(4 * ((p.w.N * p.w.K / 64 + 255) / 256)));
+  // a dual tile's wave w produces rows of the gate weight (w even) or the up
+  // weight (w odd): the choice is uniform across the wave
+  const int wsrc = DUAL ? (__builtin_amdgcn_readfirstlane(wave) & 1) : 0;
+  const NF4View& wv = wsrc ? p.w2 : p.w;
+  bf.codes = rsrc(wv.codes, (uint32_t)(wv.N * wv.K / 2));
+  bf.qscale = rsrc(wv.qscale, (uint32_t)(wv.N * wv.K / 64));
+  bf.dscale = rsrc(wv.dscale, (uint32_t)(4 * ((wv.N * wv.K / 64 + 255) / 256)));
   const uint32_t K = (uint32_t)p.w.K;
   // rows past M give offsets past the end (the host checks 32-bit room)
   const uint32_t a_base = (uint32_t)((m0 + tid / 8) * p.lda * 2) + 2 * 8 * (tid % 8);
@@ -418,7 +509,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   const uint32_t whalf = (uint32_t)(tid & 1);
   // weight block coordinates of this thread for contraction step kt
   auto w_n = [&](int64_t kt) -> uint32_t {
-    if constexpr (MODE == MODE_FWD) return (uint32_t)(j0 + wblk);
+    if constexpr (DUAL) return (uint32_t)(j0 + dual_col(wblk));
+    else if constexpr (MODE == MODE_FWD) return (uint32_t)(j0 + wblk);
     else return (uint32_t)(kt * BK + (wblk >> 2));
   };
   auto w_k = [&](int64_t kt) -> uint32_t {
@@ -463,31 +555,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   // Each wave rounds its 128 x 64 block to bf16 into its own LDS region
   // (lanes l and l^1 hold neighbouring columns of the same rows, so one DPP
   // swap per pair of values gives each lane a packed pair), then writes it
-  // back out as 16-byte row segments: 8 lanes cover one 128-byte row.  The
-  // main loop's last barrier has freed LDS; the regions are disjoint, and a
-  // wave's LDS operations complete in order, so no barrier is needed.
+  // back out as 16-byte row segments.  The main loop's last barrier has freed
+  // LDS; the regions are disjoint, and a wave's LDS operations complete in
+  // order, so no barrier is needed.  With the SwiGLU epilogue the block is
+  // 128 x 32: h = silu(g) * u of the wave's gate and up accumulators.
   u16* sE = smem + wave * E_ELEMS;
   const bool odd = lane & 1;
+  constexpr int NBLK = DUAL == DUAL_SWIGLU ? 1 : 2;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NBLK; ++b)
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
-        const float x0 = acc[a][b][v], x1 = acc[a][b][v + 1];
+        float x0 = acc[a][b][v], x1 = acc[a][b][v + 1];
+        if constexpr (DUAL == DUAL_SWIGLU) {
+          x0 = x0 / (1.0f + __expf(-x0)) * acc[a][1][v];
+          x1 = x1 / (1.0f + __expf(-x1)) * acc[a][1][v + 1];
+        }
         const float got = dpp_f32<DPP_QUAD_XOR1>(odd ? x0 : x1);
         const int row = a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3) + (odd ? 1 : 0);
         const int col = b * 32 + ((lane & 31) & ~1);
         *reinterpret_cast<uint32_t*>(sE + row * EPITCH + col) =
             odd ? pack_bf16x2(got, x1) : pack_bf16x2(x0, got);
       }
+  // read back: 8 lanes per 64-column row (4 per 32-column row)
+  constexpr int LPR = NBLK * 4;              // lanes per row
+  constexpr int RPI = 64 / LPR;              // rows per instruction
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int row = q * 8 + (lane >> 3), col = (lane & 7) * 8;
+  for (int q = 0; q < 128 / RPI; ++q) {
+    const int row = q * RPI + lane / LPR, col = (lane % LPR) * 8;
     const uint4 v = *reinterpret_cast<const uint4*>(sE + row * EPITCH + col);
-    const int64_t i = m0 + wm * 128 + row, j = j0 + wn * 64 + col;
+    const int64_t i = m0 + wm * 128 + row;
+    int64_t j;
+    u16* out;
+    if constexpr (DUAL == DUAL_SEPARATE) {
+      j = j0 + wn * 32 + (col & 31);
+      out = col < 32 ? p.out : p.out2;
+    } else if constexpr (DUAL == DUAL_SWIGLU) {
+      j = j0 + wn * 32 + col;
+      out = p.out;
+    } else {
+      j = j0 + wn * 64 + col;
+      out = p.out;
+    }
     if (i < p.M) {
-      u16* dst = p.out + i * p.ldo + j;
+      u16* dst = out + i * p.ldo + j;
       if (p.out_vec && j + 8 <= p.J) {
         *reinterpret_cast<uint4*>(dst) = v;
       } else {
@@ -504,18 +617,19 @@ static bool vec_ok(const void* ptr, int64_t ld) {
   return ((uintptr_t)ptr % 16 == 0) && (ld % 8 == 0);
 }
 
-template <int MODE>
+template <int MODE, int DUAL = DUAL_NONE>
 static hipError_t launch(const BigArgs& p, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<MODE>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<MODE, DUAL>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes<MODE>());
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((unsigned)((p.M + BM - 1) / BM), (unsigned)((p.J + BN - 1) / BN), 1);
-  hipLaunchKernelGGL(k_gemm_big<MODE>, grid, dim3(NTHREADS), lds_bytes<MODE>(), st, p);
+  const int64_t bn = DUAL ? BN / 2 : BN;
+  dim3 grid((unsigned)((p.M + BM - 1) / BM), (unsigned)((p.J + bn - 1) / bn), 1);
+  hipLaunchKernelGGL((k_gemm_big<MODE, DUAL>), grid, dim3(NTHREADS), lds_bytes<MODE>(), st, p);
   return hipGetLastError();
 }
 
@@ -534,7 +648,7 @@ hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const floa
                            const u16* B, int r, float s, u16* Y, hipStream_t st) {
   if (!big::vec_ok(X, w.K) || !fits_32bit(M, w.K, w))
     return launch_fwd_generic(w, X, M, T, B, r, s, Y, st);
-  big::BigArgs p;
+  big::BigArgs p{};
   p.a = X; p.lda = w.K; p.a_vec = big::vec_ok(X, w.K);
   p.w = w;
   p.M = M; p.J = w.N; p.C = w.K;
@@ -544,11 +658,42 @@ hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const floa
   return big::launch<big::MODE_FWD>(p, st);
 }
 
+// Gate and up projections of one X in one kernel (epilogue: 1 = both outputs,
+// 2 = bf16(silu(g) * u) into Yg).  M is cut into slices whose X fits the
+// 32-bit buffer offsets.
+hipError_t launch_fwd_dual(const NF4View& wg, const NF4View& wu, const u16* X, int64_t M,
+                           const float* Tg, const float* Tu, const u16* Bg, const u16* Bu, int r,
+                           float s, int epilogue, u16* Yg, u16* Yu, hipStream_t st) {
+  const int64_t N = wg.N, K = wg.K;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((N + big::BN) * K / 2 >= lim || N * K / 64 >= lim) return hipErrorInvalidValue;
+  int64_t mstep = (lim - 8 * big::BK * 2) / (K * 2) - big::BM;
+  mstep = mstep / big::BM * big::BM;
+  if (mstep < big::BM) return hipErrorInvalidValue;
+  for (int64_t m = 0; m < M; m += mstep) {
+    const int64_t mc = std::min(mstep, M - m);
+    big::BigArgs p{};
+    p.a = X + m * K; p.lda = K; p.a_vec = true;
+    p.w = wg; p.w2 = wu;
+    p.M = mc; p.J = N; p.C = K;
+    p.la = Tg + m * r; p.la2 = Tu + m * r;
+    p.lb = Bg; p.lb2 = Bu; p.r = r; p.s = s;
+    p.la_vec = r % 8 == 0 && big::vec_ok(Tg, 8) && big::vec_ok(Tu, 8);
+    p.lb_vec = big::vec_ok(Bg, r) && big::vec_ok(Bu, r);
+    p.out = Yg + m * N; p.out2 = epilogue == 1 ? Yu + m * N : nullptr; p.ldo = N;
+    p.out_vec = big::vec_ok(Yg, N) && (epilogue != 1 || big::vec_ok(Yu, N));
+    const hipError_t e = epilogue == 1 ? big::launch<big::MODE_FWD, big::DUAL_SEPARATE>(p, st)
+                                       : big::launch<big::MODE_FWD, big::DUAL_SWIGLU>(p, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_dx_main(const NF4View& w, const u16* dY, int64_t M, const float* U,
                           const u16* A, int r, float s, u16* dX, hipStream_t st) {
   if (!big::vec_ok(dY, w.N) || !fits_32bit(M, w.N, w) || (w.N + big::BK) * w.K / 2 >= ((int64_t)1 << 31))
     return launch_dx_generic(w, dY, M, U, A, r, s, dX, st);
-  big::BigArgs p;
+  big::BigArgs p{};
   p.a = dY; p.lda = w.N; p.a_vec = big::vec_ok(dY, w.N);
   p.w = w;
   p.M = M; p.J = w.K; p.C = w.N;

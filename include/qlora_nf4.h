@@ -154,6 +154,32 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M,
                      int compute_dtype, uint16_t* Y, float* T_save,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Epilogues of qlora_dual_fwd. */
+enum { QL_DUAL_SEPARATE = 1, QL_DUAL_SWIGLU = 2 };
+
+/* Gate and up projections of one input in one kernel.  The Transformers
+ * "Bitsandbytes" page and the Ultralytics "QLoRA" page fine-tune Llama-2
+ * models, whose MLP feeds the same X to a gate and an up projection and
+ * multiplies silu(gate) by up; with LoRA on every linear both projections
+ * are QLoRA layers.  Each output is the forward of qlora_linear_fwd on its
+ * own weight and adapter (same T, same bf16 LoRA operand, same fp32 sums):
+ *   G[m][n] = sum_k X W_gate'^T + s T_gate B_gate^T,   U likewise with _up,
+ * with the X tile read once for both weights.  epilogue QL_DUAL_SEPARATE
+ * writes Y_gate = bf16(G), Y_up = bf16(U) (H unused, may be NULL);
+ * QL_DUAL_SWIGLU writes H = bf16(silu(G) * U), silu(x) = x / (1 + e^-x)
+ * in fp32 from the fp32 sums (Y_gate, Y_up unused, may be NULL).
+ * T_gate_save, T_up_save: fp32 [M][r] (required; the inputs of each
+ * projection's qlora_linear_bwd).  w_gate and w_up must have the same shape
+ * [N][K]; other arguments as in qlora_linear_fwd (there is no decode-size
+ * special case: every M runs the tiled kernel).  workspace: device, at least
+ * qlora_fwd_workspace_bytes(M, N, K, r) bytes. */
+int qlora_dual_fwd(const qlora_nf4_weight* w_gate, const qlora_nf4_weight* w_up,
+                   const uint16_t* X, int64_t M, const uint16_t* A_gate, const uint16_t* B_gate,
+                   const uint16_t* A_up, const uint16_t* B_up, int r, float alpha,
+                   int compute_dtype, int epilogue, uint16_t* Y_gate, uint16_t* Y_up,
+                   uint16_t* H, float* T_gate_save, float* T_up_save,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace the backward needs (bytes, 256-byte granular). */
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 

@@ -160,3 +160,34 @@ def test_merge_rejects_bad_arguments():
     assert L.qlora_unmerge(None, 16, 64, FAKE, FAKE, 8, 16.0, FAKE, None) == -1
     assert L.qlora_unmerge(FAKE, 16, 64, FAKE, FAKE, 8, 16.0, FAKE + 8, None) == -4
     assert L.qlora_unmerge(FAKE, 1 << 20, 1 << 12, FAKE, FAKE, 8, 16.0, FAKE, None) == -2
+
+
+def _dual(wg, wu, X=FAKE, M=64, Ag=FAKE, Bg=FAKE, Au=FAKE, Bu=FAKE, r=8, dtype=1, epi=1, Yg=FAKE,
+          Yu=FAKE, H=FAKE, Tg=FAKE, Tu=FAKE, ws=FAKE, wsb=1 << 30):
+    return q.lib().qlora_dual_fwd(ctypes.byref(wg) if wg is not None else None,
+                                  ctypes.byref(wu) if wu is not None else None, X, M, Ag, Bg, Au, Bu,
+                                  r, 16.0, dtype, epi, Yg, Yu, H, Tg, Tu, ws, wsb, None)
+
+
+def test_dual_rejects_bad_arguments():
+    """Every check of qlora_dual_fwd fires before any launch (the pointers are
+    fake; a call that got as far as a launch would need a GPU)."""
+    wg, wu = _weight(), _weight()
+    assert _dual(None, wu) == -1
+    assert _dual(wg, None) == -1
+    assert _dual(wg, _weight(rows=128)) == -2            # shapes differ
+    assert _dual(wg, _weight(cols=320)) == -2
+    assert _dual(wg, wu, M=0) == -2
+    assert _dual(wg, wu, r=0) == -3
+    assert _dual(wg, wu, r=129) == -3
+    assert _dual(wg, wu, dtype=2) == -3
+    assert _dual(wg, wu, epi=0) == -3
+    assert _dual(wg, wu, epi=3) == -3
+    assert _dual(wg, wu, Bu=None) == -1
+    assert _dual(wg, wu, Tu=None) == -1
+    assert _dual(wg, wu, epi=1, Yu=None) == -1           # separate outputs need both
+    assert _dual(wg, wu, epi=2, H=None) == -1            # SwiGLU needs H
+    assert _dual(wg, wu, Ag=FAKE + 4) == -4
+    assert _dual(wg, wu, epi=2, H=FAKE + 2) == -4
+    assert _dual(wg, wu, M=4096, ws=None, wsb=0) == -5   # the rank-r product needs a workspace
+    assert q.lib().qlora_last_error() != b""
