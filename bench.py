@@ -472,10 +472,10 @@ def main():
     dx_ms = (kern["dx_up"] + kern["dx_down"]) / 2
     main_flops = 2 * cfg.M * up.N * up.K + 2 * cfg.M * up.N * cfg.r   # base + LoRA prologue
     if dx_ms >= fwd_ms:
-        dom, dom_ms = "k_gemm_big<1> dX (NF4 transposed producer, U A prologue)", dx_ms
+        dom, dom_ms = "k_gemm_big<1, 0> dX (NF4 transposed producer, U A prologue)", dx_ms
         dom_key = "gemm_dx"
     else:
-        dom, dom_ms = "k_gemm_big<0> fwd (NF4 producer, T B^T prologue)", fwd_ms
+        dom, dom_ms = "k_gemm_big<0, 0> fwd (NF4 producer, T B^T prologue)", fwd_ms
         dom_key = "gemm_fwd"
     achieved = main_flops / (dom_ms * 1e-3) / 1e12
     src = source_hash("gemm_big.hip")
