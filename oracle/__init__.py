@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_nf4_quantize.restype = I
         L.oracle_nf4_dequantize.argtypes = [P, P, P, I64, I64, P, I]
         L.oracle_nf4_dequantize.restype = I
+        L.oracle_int4_levels.argtypes, L.oracle_int4_levels.restype = [P], None
+        L.oracle_quantize.argtypes = [P, I64, I64, P, I, P, P, P, P, I]
+        L.oracle_quantize.restype = I
+        L.oracle_dequantize.argtypes = [P, P, P, I64, I64, P, I, P, I]
+        L.oracle_dequantize.restype = I
         L.oracle_qlora_fwd.argtypes = [P, I64, I64, P, I64, P, P, I, D, P, I64, P, P, I]
         L.oracle_qlora_fwd.restype = I
         L.oracle_qlora_bwd_dx.argtypes = [P, I64, I64, P, I64, P, P, I, D, P, I64, P, I]
@@ -163,6 +168,49 @@ def nf4_dequantize(codes, qscale, dscale, rows: int, cols: int, threads: int | N
     out = np.zeros((rows, cols), np.uint16)
     _check(lib().oracle_nf4_dequantize(_ptr(codes), _ptr(qscale), _ptr(dscale), rows, cols,
                                        _ptr(out), threads or default_threads()), "nf4_dequantize")
+    return out
+
+
+def int4_levels() -> np.ndarray:
+    out = np.zeros(16, np.float32)
+    lib().oracle_int4_levels(_ptr(out))
+    return out
+
+
+def codebook_levels(codebook: str) -> np.ndarray:
+    return {"nf4": nf4_levels, "int4": int4_levels}[codebook]()
+
+
+def quantize(W: np.ndarray, codebook: str = "nf4", double_quant: bool = True,
+             threads: int | None = None):
+    """(codes, qscale or None, dscale, absmax) with a codebook ("nf4" or "int4") and
+    the scale format: double-quantized E4M3 scales with group constants, or (double_quant
+    False) the fp32 block absmax itself in dscale [N*K/64]."""
+    W = np.ascontiguousarray(W, np.float32)
+    rows, cols = W.shape
+    nb = rows * cols // 64
+    lv = codebook_levels(codebook)
+    codes = np.zeros(rows * cols // 2, np.uint8)
+    qscale = np.zeros(nb, np.uint8) if double_quant else None
+    dscale = np.zeros((nb + 255) // 256 if double_quant else nb, np.float32)
+    absmax = np.zeros(nb, np.float32)
+    _check(lib().oracle_quantize(_ptr(W), rows, cols, _ptr(lv), int(double_quant), _ptr(codes),
+                                 _ptr(qscale), _ptr(dscale), _ptr(absmax), threads or default_threads()),
+           "quantize")
+    return codes, qscale, dscale, absmax
+
+
+def dequantize(codes, qscale, dscale, rows: int, cols: int, codebook: str = "nf4",
+               threads: int | None = None):
+    """bf16 bit patterns (uint16 [N, K]); qscale None means fp32 block scales in dscale."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    dq = qscale is not None
+    qs = np.ascontiguousarray(qscale, np.uint8) if dq else None
+    ds = np.ascontiguousarray(dscale, np.float32)
+    lv = codebook_levels(codebook)
+    out = np.zeros((rows, cols), np.uint16)
+    _check(lib().oracle_dequantize(_ptr(codes), _ptr(qs), _ptr(ds), rows, cols, _ptr(lv), int(dq),
+                                   _ptr(out), threads or default_threads()), "dequantize")
     return out
 
 

@@ -160,7 +160,8 @@ static double bf16_to_double(uint16_t h) { return (double)u2f((uint32_t)h << 16)
 /* Ultralytics "QLoRA", "How QLoRA works": one absmax scale per block of 64  */
 /* weights; each weight divided by its block's absmax and mapped to the      */
 /* nearest level.  An all-zero block has no defined quotient: it gets the    */
-/* code of the exact zero level.                                             */
+/* code that v = 0 would get (the exact zero level of NF4; for a codebook    */
+/* without zero, the nearer of the two levels around it, the lower on a tie). */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   const float* W; int64_t cols; const float* levels; uint8_t* codes; float* absmax;
@@ -168,8 +169,7 @@ typedef struct {
 
 static void enc_range(void* p, int64_t b0, int64_t b1) {
   enc_ctx* c = (enc_ctx*)p;
-  int zero_code = 0;
-  for (int i = 0; i < 16; ++i) if (c->levels[i] == 0.0f) zero_code = i;
+  const int zero_code = oracle_nearest_level(0.0f, c->levels);
   for (int64_t b = b0; b < b1; ++b) {
     const float* x = c->W + b * 64;
     float a = 0.0f;
@@ -204,18 +204,23 @@ int oracle_encode_blocks(const float* W, int64_t rows, int64_t cols,
 /* constant is d = max / 448 and each scale is stored as E4M3(absmax / d).   */
 /* The NF4 codes use the exact fp32 absmax.                                  */
 /* ------------------------------------------------------------------------ */
-int oracle_nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
-                        uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
-                        int nthreads) {
-  if (block != 64 || dq_block != 256) return -3;
-  if (!W || !codes || !qscale || !dscale || rows <= 0 || cols <= 0 || cols % 64) return -1;
+int oracle_quantize(const float* W, int64_t rows, int64_t cols, const float levels[16],
+                    int double_quant, uint8_t* codes, uint8_t* qscale, float* dscale,
+                    float* absmax_out, int nthreads) {
+  if (!W || !levels || !codes || !dscale || (double_quant && !qscale) || rows <= 0 || cols <= 0 ||
+      cols % 64)
+    return -1;
   int64_t nb = rows * cols / 64;
   float* a = (float*)malloc((size_t)nb * sizeof(float));
   if (!a) return -1;
-  float L[16];
-  oracle_nf4_levels(L);
-  int rc = oracle_encode_blocks(W, rows, cols, L, codes, a, nthreads);
+  int rc = oracle_encode_blocks(W, rows, cols, levels, codes, a, nthreads);
   if (rc) { free(a); return rc; }
+  if (!double_quant) {                            /* the block scales kept as fp32 */
+    memcpy(dscale, a, (size_t)nb * sizeof(float));
+    if (absmax_out) memcpy(absmax_out, a, (size_t)nb * sizeof(float));
+    free(a);
+    return 0;
+  }
   int64_t ng = (nb + 255) / 256;
   for (int64_t g = 0; g < ng; ++g) {
     int64_t b0 = g * 256, b1 = b0 + 256 < nb ? b0 + 256 : nb;
@@ -231,6 +236,24 @@ int oracle_nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, i
   return 0;
 }
 
+int oracle_nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
+                        uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
+                        int nthreads) {
+  if (block != 64 || dq_block != 256) return -3;
+  if (!qscale) return -1;
+  float L[16];
+  oracle_nf4_levels(L);
+  return oracle_quantize(W, rows, cols, L, 1, codes, qscale, dscale, absmax_out, nthreads);
+}
+
+/* INT4, the comparison codebook of the Ultralytics "QLoRA" encoding snippet:
+ * 16 evenly spaced levels on [-1, 1], L[i] = -1 + 2 i / 15, each rounded once
+ * to fp32 (the quotient (2 i - 15) / 15 is formed in double; no value lies
+ * near enough to an fp32 midpoint for the double step to matter). */
+void oracle_int4_levels(float out[16]) {
+  for (int i = 0; i < 16; ++i) out[i] = (float)((double)(2 * i - 15) / 15.0);
+}
+
 /* ------------------------------------------------------------------------ */
 /* O7: dequantize.  Ultralytics "QLoRA", "How QLoRA works": a weight is      */
 /* restored as level[code] times its block scale, and the forward pass uses  */
@@ -239,14 +262,16 @@ int oracle_nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, i
 /* ------------------------------------------------------------------------ */
 typedef struct {
   const uint8_t* codes; const uint8_t* qscale; const float* dscale; int64_t cols;
-  uint16_t* out; float L[16];
+  uint16_t* out; float L[16]; int double_quant;
 } deq_ctx;
 
 static void deq_range(void* p, int64_t b0, int64_t b1) {
   deq_ctx* c = (deq_ctx*)p;
   for (int64_t b = b0; b < b1; ++b) {
-    /* E4M3 value (4 significant bits) times an fp32: exact in double, then rounded once */
-    float s = (float)(oracle_e4m3_value(c->qscale[b]) * (double)c->dscale[b / 256]);
+    /* E4M3 value (4 significant bits) times an fp32: exact in double, then
+     * rounded once; without double quantization the fp32 scale itself */
+    float s = c->double_quant ? (float)(oracle_e4m3_value(c->qscale[b]) * (double)c->dscale[b / 256])
+                              : c->dscale[b];
     for (int e = 0; e < 64; ++e) {
       uint8_t byte = c->codes[b * 32 + e / 2];
       int code = (e & 1) ? (byte >> 4) : (byte & 15);
@@ -256,14 +281,26 @@ static void deq_range(void* p, int64_t b0, int64_t b1) {
   }
 }
 
-int oracle_nf4_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
-                          int64_t rows, int64_t cols, uint16_t* out_bf16, int nthreads) {
-  if (!codes || !qscale || !dscale || !out_bf16 || rows <= 0 || cols <= 0 || cols % 64) return -1;
+int oracle_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
+                      int64_t rows, int64_t cols, const float levels[16], int double_quant,
+                      uint16_t* out_bf16, int nthreads) {
+  if (!codes || (double_quant && !qscale) || !dscale || !levels || !out_bf16 || rows <= 0 ||
+      cols <= 0 || cols % 64)
+    return -1;
   deq_ctx c;
   c.codes = codes; c.qscale = qscale; c.dscale = dscale; c.cols = cols; c.out = out_bf16;
-  oracle_nf4_levels(c.L);
+  c.double_quant = double_quant;
+  memcpy(c.L, levels, sizeof(c.L));
   parallel_for(rows * cols / 64, nthreads, deq_range, &c);
   return 0;
+}
+
+int oracle_nf4_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
+                          int64_t rows, int64_t cols, uint16_t* out_bf16, int nthreads) {
+  if (!qscale) return -1;
+  float L[16];
+  oracle_nf4_levels(L);
+  return oracle_dequantize(codes, qscale, dscale, rows, cols, L, 1, out_bf16, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -74,6 +74,26 @@ int oracle_nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, i
 int oracle_nf4_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
                           int64_t rows, int64_t cols, uint16_t* out_bf16, int nthreads);
 
+/* The 16 INT4 levels of the Ultralytics "QLoRA" snippet's comparison: evenly
+ * spaced on [-1, 1], L[i] = fl32(-1 + 2 i / 15). */
+void oracle_int4_levels(float out[16]);
+
+/* Quantization with a caller-given codebook and scale format.  Transformers
+ * "Bitsandbytes" (4-bit section): double quantization of the scales is an
+ * option.  double_quant = 1: as oracle_nf4_quantize with these levels.
+ * double_quant = 0: dscale [N*K/64] receives each block's exact fp32 absmax
+ * and qscale is unused (may be NULL).  An all-zero block gets the code of
+ * v = 0 (nearest level, lower code on a tie). */
+int oracle_quantize(const float* W, int64_t rows, int64_t cols, const float levels[16],
+                    int double_quant, uint8_t* codes, uint8_t* qscale, float* dscale,
+                    float* absmax_out, int nthreads);
+
+/* Dequantize with a caller-given codebook: w' = bf16(fl32(L[code] * s_b)),
+ * s_b = fl32(E4M3(q_b) * d_g) (double_quant = 1) or the fp32 dscale[b] (0). */
+int oracle_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
+                      int64_t rows, int64_t cols, const float levels[16], int double_quant,
+                      uint16_t* out_bf16, int nthreads);
+
 /* Forward, for the rows listed in row_idx (or all M rows if row_idx == NULL):
  *   T[m,j] = sum_k X[m,k] A[j,k]
  *   Y[m,n] = sum_k X[m,k] W'[n,k] + (alpha/r) sum_j T[m,j] B[n,j]

@@ -529,3 +529,100 @@ def test_swiglu_closed_forms(orc):
     assert orc.swiglu(np.array([50.0]), np.array([1.0]))[0] == pytest.approx(50.0, rel=1e-15)
     u = rng.normal(size=g.shape)
     assert np.allclose(orc.swiglu(g, 3.0 * u), 3.0 * orc.swiglu(g, u), rtol=1e-14, atol=1e-300)
+
+
+# --------------------------------------------------------------------------
+# Codebook and scale-format variants: the INT4 comparison codebook of the
+# Ultralytics snippet, and block scales kept in fp32 (no double quantization)
+# --------------------------------------------------------------------------
+def _f32_nearest(fr: Fraction) -> np.float32:
+    """The fp32 value nearest to an exact rational (ties to even), by search."""
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-2)), f, np.nextafter(f, np.float32(2))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(c.view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_int4_table_is_evenly_spaced_rounded_once(orc):
+    """Sixteen levels from -1 to 1 in equal steps of 2/15, each the exact value
+    rounded once to fp32; symmetric, with no zero level."""
+    L = orc.int4_levels()
+    for i in range(16):
+        assert L[i] == _f32_nearest(Fraction(2 * i - 15, 15)), i
+    assert L[0] == -1.0 and L[15] == 1.0
+    assert np.array_equal(L[::-1], -L)
+    assert not np.any(L == 0)
+    assert np.all(np.diff(L.astype(np.float64)) > 0)
+
+
+def test_int4_snippet_mse_with_oracle_table(orc):
+    """The snippet's printed INT4 MSE (4.053e-06) also holds with the oracle's own
+    INT4 table, so the table used by the variant kernels is the compared one."""
+    torch = pytest.importorskip("torch")
+    gold = json.load(open(os.path.join(GOLDEN, "snippet_mse.json")))
+    torch.manual_seed(0)
+    w = (torch.randn(4096, 64) * 0.02).numpy()
+    L = orc.int4_levels()
+    codes, qs, ds, am = orc.quantize(w, "int4", double_quant=False)
+    assert qs is None and np.array_equal(ds, np.abs(w).max(axis=1))
+    c = np.empty(w.size, np.int64)
+    c[0::2], c[1::2] = codes & 15, codes >> 4
+    restored = L[c].reshape(w.shape) * ds[:, None]
+    assert f"{float(np.mean((restored - w).astype(np.float64) ** 2)):.3e}" == gold["int4_mse_printed"]
+
+
+def test_int4_nearest_level_matches_exact_rational_rule(orc):
+    """With the INT4 table the fp32-distance argmin equals the exact rational
+    nearest level, lower code on an exact tie; all-zero blocks take code 7, the
+    lower of the two levels nearest zero."""
+    L = orc.int4_levels()
+    Lq = [Fraction(float(x)) for x in L]
+    rng = np.random.default_rng(77)
+    mids = [np.float32((float(L[j]) + float(L[j + 1])) / 2) + np.arange(-4, 5, dtype=np.float32) *
+            np.spacing(np.float32(1.0)) for j in range(15)]
+    v = np.concatenate([rng.uniform(-1, 1, 3000).astype(np.float32), *mids]).astype(np.float32)
+    for x in v:
+        xq = Fraction(float(x))
+        d = [abs(xq - q) for q in Lq]
+        # fp32 distances decide: skip values whose two nearest fp32 distances round equal
+        df = sorted(abs(np.float32(x) - L))
+        if df[0] == df[1] and min(d) != sorted(d)[1]:
+            continue
+        ref = min(range(16), key=lambda i: (d[i], i))
+        assert orc.nearest_level(float(x), L) == ref, x
+    W = np.zeros((2, 128), np.float32)
+    W[1, 64:] = 0.5
+    for dq in (True, False):
+        codes, _, _, _ = orc.quantize(W, "int4", double_quant=dq)
+        assert np.all(codes[:64] == 0x77)
+
+
+@pytest.mark.parametrize("codebook", ["nf4", "int4"])
+@pytest.mark.parametrize("dq", [True, False])
+def test_variant_dequant_error_bound_and_self_codes(orc, codebook, dq):
+    """For every codebook and scale format: |w' - w| <= half the largest level gap
+    times the block absmax, plus the scale's own error, plus half a bf16 ulp; a
+    block holding the levels times 2^e comes back as bf16 of the levels times 2^e
+    (rounded by torch), code for code."""
+    torch = pytest.importorskip("torch")
+    L = orc.codebook_levels(codebook).astype(np.float64)
+    cfg = si.custom(N=96, K=256, M=1, r=8, seed=9, outlier_frac=0.01)
+    W = si.weight(cfg, 0)
+    codes, qs, ds, am = orc.quantize(W, codebook, double_quant=dq)
+    deq = si.bf16_bits_to_f32(orc.dequantize(codes, qs, ds, *W.shape, codebook=codebook)).astype(np.float64)
+    a = np.repeat(am.astype(np.float64), 64).reshape(W.shape)
+    if dq:
+        sc = np.repeat(np.array([orc.e4m3_value(int(q)) for q in qs]) *
+                       np.repeat(ds.astype(np.float64), 256)[:qs.size], 64).reshape(W.shape)
+    else:
+        assert np.array_equal(ds, am)
+        sc = a
+    bound = np.max(np.diff(L)) / 2 * a + np.abs(sc - a) + np.abs(deq) * 2.0 ** -8
+    assert np.all(np.abs(deq - W) <= bound + 1e-12)
+    Lf = orc.codebook_levels(codebook)
+    for e in (-9, 0, 4):
+        blk = (np.tile(Lf, 4) * np.float32(2.0 ** e)).astype(np.float32).reshape(1, 64)
+        c2, q2, d2, _ = orc.quantize(blk, codebook, double_quant=dq)
+        got = orc.dequantize(c2, q2, d2, 1, 64, codebook=codebook)
+        want = torch.from_numpy(blk).bfloat16().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want), (codebook, dq, e)
