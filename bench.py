@@ -304,6 +304,52 @@ def bench_dual(hip, lay, reps=10):
     return res
 
 
+def bench_formats(hip, lay, reps=10):
+    """Codebook and scale-format variants on the up projection (28672x8192,
+    4096 tokens, r=64): quantize and dequantize bandwidth and the fused
+    forward, for INT4 with E4M3 scales and for NF4 with fp32 block scales.
+    Algorithmic bytes per weight: quantize 4 read + 0.5 + scale bytes written
+    (1/64 + 4/16384 with double quantization, 4/64 without); dequantize the
+    reverse plus 2 written."""
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    st = torch.cuda.current_stream().cuda_stream
+    nk = lay.N * lay.K
+    fwd, _ = linear_flops(lay.M, lay.N, lay.K, lay.r)
+    out = torch.empty(lay.N, lay.K, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for _ in range(reps):
+            fn()
+        hip.record(e1, st)
+        return hip.elapsed_ms(e0, e1) / reps
+
+    res = []
+    for codebook, dq in (("int4", True), ("nf4", False)):
+        w = q.NF4Weight.empty(lay.N, lay.K, codebook=codebook, double_quant=dq)
+        scale_b = (1 / 64 + 4 / 16384) if dq else 4 / 64
+        qms = timed(lambda: q.nf4_quantize(lay.W, out=w, codebook=codebook, double_quant=dq))
+        dms = timed(lambda: q.nf4_dequantize(w, out=out))
+        fms = timed(lambda: q.qlora_linear_fwd(w, lay.X, lay.A, lay.B, lay.alpha, Y=lay.Y, T=lay.T,
+                                               workspace=lay.wsf))
+        qb, db = nk * (4 + 0.5 + scale_b), nk * (0.5 + scale_b + 2)
+        res.append({"format": f"{codebook}, {'E4M3 double-quantized' if dq else 'fp32'} scales",
+                    "quantize_us": round(qms * 1e3, 1),
+                    "quantize_frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "dequantize_us": round(dms * 1e3, 1),
+                    "dequantize_frac_hbm": round(db / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "fwd_ms": round(fms, 4), "fwd_TFLOP/s": round(fwd / (fms * 1e-3) / 1e12, 1)})
+        del w
+    del out
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_library_reference(hip, layers, reps=10):
     """Context only, not part of the path: a dense bf16 matmul from the vendor
     library (torch -> hipBLASLt) on the same shapes as the two fused forward
@@ -513,6 +559,8 @@ def main():
         extras["merge"] = bw
         log("[bench] gate/up dual projection")
         extras["dual"] = bench_dual(hip, up)
+        log("[bench] codebook and scale-format variants")
+        extras["formats"] = bench_formats(hip, up)
         log("[bench] library reference")
         extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
 

@@ -21,6 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
 
 QL_DTYPE_BF16 = 1
+QL_CODEBOOK_NF4 = 0
+QL_CODEBOOK_INT4 = 1
+CODEBOOKS = {"nf4": QL_CODEBOOK_NF4, "int4": QL_CODEBOOK_INT4}
 QL_DUAL_SEPARATE = 1
 QL_DUAL_SWIGLU = 2
 QLORA_MAX_RANK = 128
@@ -39,7 +42,7 @@ class QLoRAError(RuntimeError):
 class _Weight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
                 ("dscale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
-                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32), ("codebook", ctypes.c_int32)]
 
 
 def lib() -> ctypes.CDLL:
@@ -59,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.nf4_storage_bytes.restype = I
     L.nf4_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P, P]
     L.nf4_quantize.restype = I
+    L.qlora_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P, P]
+    L.qlora_quantize.restype = I
+    L.qlora_codebook_levels.argtypes = [I, P]
+    L.qlora_codebook_levels.restype = I
     L.nf4_dequantize.argtypes = [WP, P, P]
     L.nf4_dequantize.restype = I
     L.qlora_fwd_workspace_bytes.argtypes = [I64, I64, I64, I]
@@ -120,6 +127,13 @@ def nf4_levels():
     return list(buf)
 
 
+def codebook_levels(codebook: str = "nf4"):
+    """The 16 fp32 levels of a codebook ("nf4" or "int4") in code order."""
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qlora_codebook_levels(CODEBOOKS[codebook], ctypes.cast(buf, ctypes.c_void_p)))
+    return list(buf)
+
+
 def nf4_storage_bytes(rows: int, cols: int, block: int = 64, dq_block: int = 256):
     c, q, d = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib().nf4_storage_bytes(rows, cols, block, dq_block, ctypes.byref(c), ctypes.byref(q),
@@ -129,36 +143,51 @@ def nf4_storage_bytes(rows: int, cols: int, block: int = 64, dq_block: int = 256
 
 @dataclasses.dataclass
 class NF4Weight:
-    """A quantized frozen weight [rows][cols] held in device tensors."""
-    codes: "torch.Tensor"    # uint8 [rows*cols/2]
-    qscale: "torch.Tensor"   # uint8 [rows*cols/64]
-    dscale: "torch.Tensor"   # float32 [ceil(nb/256)]
+    """A quantized frozen weight [rows][cols] held in device tensors.  With
+    double_quant the block scales are E4M3 bytes in qscale and group constants
+    in dscale; without, qscale is None and dscale holds the fp32 block scales."""
+    codes: "torch.Tensor"              # uint8 [rows*cols/2]
+    qscale: Optional["torch.Tensor"]   # uint8 [rows*cols/64], or None
+    dscale: "torch.Tensor"             # float32 [ceil(nb/256)], or [nb]
     rows: int
     cols: int
+    codebook: str = "nf4"
+
+    @property
+    def double_quant(self) -> bool:
+        return self.qscale is not None
 
     def descriptor(self) -> _Weight:
-        return _Weight(self.codes.data_ptr(), self.qscale.data_ptr(), self.dscale.data_ptr(),
-                       self.rows, self.cols, 64, 256)
+        return _Weight(self.codes.data_ptr(), _ptr(self.qscale), self.dscale.data_ptr(),
+                       self.rows, self.cols, 64, 256 if self.double_quant else 0,
+                       CODEBOOKS[self.codebook])
 
     @staticmethod
-    def empty(rows: int, cols: int, device="cuda") -> "NF4Weight":
+    def empty(rows: int, cols: int, device="cuda", codebook: str = "nf4",
+              double_quant: bool = True) -> "NF4Weight":
         import torch
-        c, q, d = nf4_storage_bytes(rows, cols)
+        c, q, d = nf4_storage_bytes(rows, cols, 64, 256 if double_quant else 0)
         return NF4Weight(torch.empty(c, dtype=torch.uint8, device=device),
-                         torch.empty(q, dtype=torch.uint8, device=device),
-                         torch.empty(d // 4, dtype=torch.float32, device=device), rows, cols)
+                         torch.empty(q, dtype=torch.uint8, device=device) if double_quant else None,
+                         torch.empty(d // 4, dtype=torch.float32, device=device), rows, cols, codebook)
 
 
-def nf4_quantize(W, out: Optional[NF4Weight] = None, absmax=None, stream=None) -> NF4Weight:
-    """Quantize a cuda fp32 [rows, cols] weight.  ``absmax`` (optional cuda fp32
-    [rows*cols/64]) receives the exact block scales."""
+def nf4_quantize(W, out: Optional[NF4Weight] = None, absmax=None, stream=None,
+                 codebook: str = "nf4", double_quant: bool = True) -> NF4Weight:
+    """Quantize a cuda fp32 [rows, cols] weight with a codebook ("nf4" or "int4"),
+    with double-quantized scales (default) or fp32 block scales.  ``absmax``
+    (optional cuda fp32 [rows*cols/64]) receives the exact block scales."""
     import torch
     rows, cols = W.shape
     _need(W, torch.float32, (rows, cols), "W")
-    w = out if out is not None else NF4Weight.empty(rows, cols, W.device)
-    _check(lib().nf4_quantize(W.data_ptr(), rows, cols, 64, 256, w.codes.data_ptr(),
-                              w.qscale.data_ptr(), w.dscale.data_ptr(), _ptr(absmax),
-                              _stream(stream)))
+    if out is None:
+        out = NF4Weight.empty(rows, cols, W.device, codebook, double_quant)
+    w = out
+    if w.codebook != codebook or w.double_quant != double_quant:
+        raise ValueError("out has another codebook or scale format")
+    _check(lib().qlora_quantize(W.data_ptr(), rows, cols, CODEBOOKS[codebook],
+                                256 if double_quant else 0, w.codes.data_ptr(), _ptr(w.qscale),
+                                w.dscale.data_ptr(), _ptr(absmax), _stream(stream)))
     return w
 
 

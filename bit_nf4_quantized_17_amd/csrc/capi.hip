@@ -53,13 +53,17 @@ constexpr int64_t kMaxGridY = 65535;
 
 int check_weight(const qlora_nf4_weight* w) {
   if (!w) return fail(QL_ERR_NULL, "weight descriptor is NULL");
-  if (!w->codes || !w->qscale || !w->dscale) return fail(QL_ERR_NULL, "weight buffer is NULL");
-  if (w->block != 64 || w->dq_block != 256)
-    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (only 64 and 256)", w->block, w->dq_block);
+  if (w->block != 64 || (w->dq_block != 256 && w->dq_block != 0))
+    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (block 64; dq_block 256, or 0 for fp32 scales)",
+                w->block, w->dq_block);
+  if (w->codebook != QL_CODEBOOK_NF4 && w->codebook != QL_CODEBOOK_INT4)
+    return fail(QL_ERR_UNSUPPORTED, "codebook=%d", w->codebook);
+  if (!w->codes || (w->dq_block && !w->qscale) || !w->dscale)
+    return fail(QL_ERR_NULL, "weight buffer is NULL");
   if (w->rows <= 0 || w->cols <= 0 || w->cols % 64)
     return fail(QL_ERR_SHAPE, "weight shape %lld x %lld (need positive, cols %% 64 == 0)",
                 (long long)w->rows, (long long)w->cols);
-  if (!aligned16(w->codes) || !aligned16(w->qscale) || !aligned16(w->dscale))
+  if (!aligned16(w->codes) || (w->dq_block && !aligned16(w->qscale)) || !aligned16(w->dscale))
     return fail(QL_ERR_ALIGN, "weight buffers must be 16-byte aligned");
   return QL_OK;
 }
@@ -67,7 +71,10 @@ int check_weight(const qlora_nf4_weight* w) {
 NF4View view(const qlora_nf4_weight* w) {
   NF4View v;
   v.codes = w->codes;
-  v.qscale = w->qscale;
+  v.qscale = w->dq_block ? w->qscale : nullptr;
+  v.fp32_scale = w->dq_block == 0;
+  const uint32_t* bits = codebook_bits(w->codebook);
+  for (int i = 0; i < 16; ++i) std::memcpy(&v.lv[i], &bits[i], 4);
   v.dscale = w->dscale;
   v.N = w->rows;
   v.K = w->cols;
@@ -131,35 +138,56 @@ void nf4_levels(float out[16]) {
   for (int i = 0; i < 16; ++i) std::memcpy(&out[i], &kNF4LevelBits[i], 4);
 }
 
+int qlora_codebook_levels(int codebook, float out[16]) {
+  if (codebook != QL_CODEBOOK_NF4 && codebook != QL_CODEBOOK_INT4)
+    return fail(QL_ERR_UNSUPPORTED, "codebook=%d", codebook);
+  if (!out) return fail(QL_ERR_NULL, "output is NULL");
+  const uint32_t* bits = codebook_bits(codebook);
+  for (int i = 0; i < 16; ++i) std::memcpy(&out[i], &bits[i], 4);
+  return ok();
+}
+
 int nf4_storage_bytes(int64_t rows, int64_t cols, int block, int dq_block, size_t* codes_bytes,
                       size_t* qscale_bytes, size_t* dscale_bytes) {
-  if (block != 64 || dq_block != 256)
-    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (only 64 and 256)", block, dq_block);
+  if (block != 64 || (dq_block != 256 && dq_block != 0))
+    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (block 64; dq_block 256, or 0 for fp32 scales)",
+                block, dq_block);
   if (rows <= 0 || cols <= 0 || cols % 64)
     return fail(QL_ERR_SHAPE, "shape %lld x %lld (need positive, cols %% 64 == 0)",
                 (long long)rows, (long long)cols);
   const int64_t nb = rows * cols / 64;
   if (codes_bytes) *codes_bytes = (size_t)(rows * cols / 2);
-  if (qscale_bytes) *qscale_bytes = (size_t)nb;
-  if (dscale_bytes) *dscale_bytes = (size_t)((nb + 255) / 256) * sizeof(float);
+  if (qscale_bytes) *qscale_bytes = dq_block ? (size_t)nb : 0;
+  if (dscale_bytes) *dscale_bytes = (size_t)(dq_block ? (nb + 255) / 256 : nb) * sizeof(float);
   return ok();
 }
 
-int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
-                 uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out, void* stream) {
-  if (block != 64 || dq_block != 256)
-    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (only 64 and 256)", block, dq_block);
-  if (!W || !codes || !qscale || !dscale) return fail(QL_ERR_NULL, "a required pointer is NULL");
+int qlora_quantize(const float* W, int64_t rows, int64_t cols, int codebook, int dq_block,
+                   uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out, void* stream) {
+  if (dq_block != 256 && dq_block != 0)
+    return fail(QL_ERR_UNSUPPORTED, "dq_block=%d (256, or 0 for fp32 scales)", dq_block);
+  if (codebook != QL_CODEBOOK_NF4 && codebook != QL_CODEBOOK_INT4)
+    return fail(QL_ERR_UNSUPPORTED, "codebook=%d", codebook);
+  if (!W || !codes || (dq_block && !qscale) || !dscale) return fail(QL_ERR_NULL, "a required pointer is NULL");
   if (rows <= 0 || cols <= 0 || cols % 64)
     return fail(QL_ERR_SHAPE, "shape %lld x %lld (need positive, cols %% 64 == 0)",
                 (long long)rows, (long long)cols);
   if ((rows * cols / 64 + 255) / 256 > 0x7fffffffLL) return fail(QL_ERR_SHAPE, "weight too large");
-  if (!aligned16(W) || !aligned16(codes) || !aligned16(qscale) || !aligned16(dscale) ||
+  if (!aligned16(W) || !aligned16(codes) || (dq_block && !aligned16(qscale)) || !aligned16(dscale) ||
       (absmax_out && !aligned16(absmax_out)))
     return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  return hip_status(launch_quantize(W, rows, cols, codes, qscale, dscale, absmax_out,
-                                    (hipStream_t)stream),
-                    "nf4_quantize launch");
+  return hip_status(launch_quantize(W, rows, cols, codebook, dq_block == 0, codes, qscale, dscale,
+                                    absmax_out, (hipStream_t)stream),
+                    "qlora_quantize launch");
+}
+
+int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
+                 uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out, void* stream) {
+  if (block != 64 || (dq_block != 256 && dq_block != 0))
+    return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (block 64; dq_block 256, or 0 for fp32 scales)",
+                block, dq_block);
+  return qlora_quantize(W, rows, cols, QL_CODEBOOK_NF4, dq_block, codes, qscale, dscale, absmax_out,
+                        stream);
 }
 
 int nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, void* stream) {

@@ -25,23 +25,57 @@ constexpr uint32_t kNF4LevelBits[16] = {
     0x3da2fb03u, 0x3e24cae1u, 0x3e7c04dcu, 0x3ead0338u,
     0x3ee1a4b7u, 0x3f1007aau, 0x3f3913b1u, 0x3f800000u};
 
+// The comparison codebook of the same snippet: 16 evenly spaced levels on
+// [-1, 1], L[i] = -1 + 2 i / 15 rounded once to fp32 (no zero level).
+constexpr uint32_t kINT4LevelBits[16] = {
+    0xbf800000u, 0xbf5ddddeu, 0xbf3bbbbcu, 0xbf19999au,
+    0xbeeeeeefu, 0xbeaaaaabu, 0xbe4ccccdu, 0xbd888889u,
+    0x3d888889u, 0x3e4ccccdu, 0x3eaaaaabu, 0x3eeeeeefu,
+    0x3f19999au, 0x3f3bbbbcu, 0x3f5ddddeu, 0x3f800000u};
+
+enum Codebook { CODEBOOK_NF4 = 0, CODEBOOK_INT4 = 1 };
+inline const uint32_t* codebook_bits(int codebook) {
+  return codebook == CODEBOOK_INT4 ? kINT4LevelBits : kNF4LevelBits;
+}
+
+// A quantized weight as the kernels see it.  With fp32_scale the block
+// scales are the exact fp32 absmax values in dscale[b] (no double
+// quantization, qscale unused); otherwise s_b = fl32(E4M3(qscale[b]) *
+// dscale[b / 256]).  lv holds the codebook's 16 levels.
 struct NF4View {
   const uint8_t* codes;
   const uint8_t* qscale;
   const float* dscale;
   int64_t N, K;
+  bool fp32_scale;
+  float lv[16];
 };
+
+// The kernels restore a block scale as fl32(E4M3(q) * d) everywhere.  For
+// fp32 scales they read q from an empty buffer (0) and OR in the E4M3 code of
+// 1.0, and d from dscale[blk >> 0] instead of dscale[blk >> 8]; the product is
+// then the stored fp32 scale exactly.
+constexpr uint32_t kE4M3One = 0x38u;
+inline uint32_t scale_q_or(const NF4View& w) { return w.fp32_scale ? kE4M3One : 0u; }
+inline uint32_t scale_d_shift(const NF4View& w) { return w.fp32_scale ? 0u : 8u; }
+inline int64_t scale_d_count(const NF4View& w) {
+  const int64_t nb = w.N * w.K / 64;
+  return w.fp32_scale ? nb : (nb + 255) / 256;
+}
 
 // Decision points of the nearest-level rule: cut[j] is the smallest fp32 v
 // with fl32(L[j+1] - v) < fl32(v - L[j]), so the code of v in [-1, 1] is the
 // number of cut[j] <= v (ties go to the lower code, as argmin does).
 struct EncodeCuts {
   float cut[15];
+  int zero_code;   // the code of v = 0, given to an all-zero block
 };
-const EncodeCuts& encode_cuts();
+const EncodeCuts& encode_cuts(int codebook);
 
-hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
-                           uint8_t* qscale, float* dscale, float* absmax, hipStream_t s);
+// fp32_scale: dscale receives the nb fp32 block scales (qscale unused)
+hipError_t launch_quantize(const float* W, int64_t N, int64_t K, int codebook, bool fp32_scale,
+                           uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax,
+                           hipStream_t s);
 hipError_t launch_dequantize(const NF4View& w, u16* out, hipStream_t s);
 
 // ---- GEMM family (gemm.hip) ----

@@ -317,11 +317,12 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   {
     // word e holds the pair (byte & 15, byte >> 4) of byte e / 64: thread tid
     // writes bytes tid/64 + 8i, whose low nibble is tid/64 or tid/64 + 8
-    const float lo0 = __uint_as_float(kNF4LevelBits[wsc]);
-    const float lo1 = __uint_as_float(kNF4LevelBits[wsc + 8]);
+    // levels of the weight's codebook (kernel arguments, scalar loads)
+    const float lo0 = p.w.lv[wsc];
+    const float lo1 = p.w.lv[wsc + 8];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
-      lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, __uint_as_float(kNF4LevelBits[i >> 1]));
+      lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, p.w.lv[i >> 1]);
   }
   float* ttab = reinterpret_cast<float*>(smem + L.ttab);
 
@@ -746,8 +747,9 @@ bool decode_fits(int64_t M, const NF4View& w, int r) {
   if (!(M >= 1 && M <= 16 && w.N * w.K / 2 < lim && 16 * w.K * 2 < lim && (int64_t)r * w.K * 2 < lim &&
         w.N * r * 2 < lim && (dec::MAX_KPARTS - 1) * M * w.N < lim))
     return false;
-  // K a multiple of 256 keeps every wave's scale loads 4-byte aligned
-  return (w.K / 64) % 4 == 0 && dec::plan(w.N, w.K, r).tiles > 0;
+  // K a multiple of 256 keeps every wave's scale loads 4-byte aligned; the
+  // kernel stages 8-bit block scales, so fp32 scales take the tiled path
+  return !w.fp32_scale && (w.K / 64) % 4 == 0 && dec::plan(w.N, w.K, r).tiles > 0;
 }
 
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,

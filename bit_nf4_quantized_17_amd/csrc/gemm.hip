@@ -200,8 +200,9 @@ __device__ __forceinline__ void dequant32(const uint4& c, float sc, const float*
   }
 }
 
+// restored block scale: fl32(E4M3(q) * d), or the stored fp32 scale
 __device__ __forceinline__ float block_scale(const NF4View& w, int64_t blk) {
-  return e4m3_decode(w.qscale[blk]) * w.dscale[blk >> 8];
+  return w.fp32_scale ? w.dscale[blk] : e4m3_decode(w.qscale[blk]) * w.dscale[blk >> 8];
 }
 
 // NF4 weight, rows j = n (128 of them), contraction c = k (one 64-block):
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
   const int64_t cs0 = (int64_t)blockIdx.z * p.c_per_split;
   const int64_t cs1 = min(p.C, cs0 + p.c_per_split);
 
-  if (tid < 16) sL[tid] = __uint_as_float(kNF4LevelBits[tid]);
+  if (tid < 16) sL[tid] = p.w.lv[tid];   // the weight's codebook (unused without a weight)
 
   f32x16_t acc[TM][TN];
 #pragma unroll

@@ -101,12 +101,10 @@ struct Table {
   uint32_t lo[4], hi[4];   // low / high bytes of the 16 bf16 values, 4 per word
 };
 
-__device__ __forceinline__ Table make_table(float sc) {
+__device__ __forceinline__ Table make_table(const float (&lv)[16], float sc) {
   uint32_t P[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    P[j] = pack_bf16x2(__uint_as_float(kNF4LevelBits[2 * j]) * sc,
-                       __uint_as_float(kNF4LevelBits[2 * j + 1]) * sc);
+  for (int j = 0; j < 8; ++j) P[j] = pack_bf16x2(lv[2 * j] * sc, lv[2 * j + 1] * sc);
   Table t;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -140,10 +138,6 @@ __device__ __forceinline__ void dequant8(const Table& t, uint32_t c, uint32_t o[
   o[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);
 }
 
-__device__ __forceinline__ float block_scale(const NF4View& w, int64_t blk) {
-  return e4m3_decode(w.qscale[blk]) * w.dscale[blk >> 8];
-}
-
 // ---------------------------------------------------------------------------
 // Main-loop operand loads go through buffer resources: a load whose byte
 // offset is past the buffer's end returns zeros, so rows beyond M, rows of W
@@ -156,6 +150,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 struct Bufs {
   __amdgpu_buffer_rsrc_t a, codes, qscale, dscale;
+  uint32_t qor, dshift;   // scale format: E4M3 code OR-ed in, group shift of dscale
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -188,10 +183,14 @@ __device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, ui
   st.q = __builtin_amdgcn_raw_buffer_load_b8(b.qscale, blk, 0, 0);
   // a dead stage reads past the end of the group constants, which returns 0
   st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                       b.dscale, live ? 4 * (blk >> 8) : 0xFFFFFFF0u, 0, 0));
+                                       b.dscale, live ? 4 * (blk >> b.dshift) : 0xFFFFFFF0u, 0, 0));
 }
 
-__device__ __forceinline__ float stage_scale(const StageW& st) { return e4m3_decode(st.q) * st.d; }
+// fl32(E4M3(q) * d); with fp32 scales q reads 0 from an empty buffer and the
+// OR makes it E4M3(1.0), so the product is the stored scale exactly
+__device__ __forceinline__ float stage_scale(const StageW& st, uint32_t qor) {
+  return e4m3_decode(st.q | qor) * st.d;
+}
 
 __device__ __forceinline__ void store_a(const StageA& st, u16* sA, int tid) {
 #pragma unroll
@@ -264,8 +263,9 @@ __device__ __forceinline__ u16* w_dst(u16* sB, int tid) {
 }
 
 // dequantize the thread's half block and store its 32 bf16 values at dst
-__device__ __forceinline__ void store_w(const StageW& st, u16* dst) {
-  const Table t = make_table(stage_scale(st));
+__device__ __forceinline__ void store_w(const StageW& st, const float (&lv)[16], uint32_t qor,
+                                        u16* dst) {
+  const Table t = make_table(lv, stage_scale(st, qor));
   const uint32_t c[4] = {st.c.x, st.c.y, st.c.z, st.c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -404,17 +404,18 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
                                                const u16* sB, int wm, int wn, int lane,
                                                StageA& ra, StageW& w,
                                                u16* sA_next, u16* wdst_next, int tid,
-                                               const NextLoads& nl) {
+                                               const NextLoads& nl, const float (&lv)[16]) {
   bf16x8_t fa[2][4], fb[2][2];
   frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
-  const Table t = make_table(stage_scale(w));
+  const Table t = make_table(lv, stage_scale(w, nl.bf->qor));
   const uint32_t c[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
   {
     // the scale byte and group constant of the weight block after next
     const uint32_t blk = nl.wn * (nl.K / 64) + nl.wk / 64;
     w.q = __builtin_amdgcn_raw_buffer_load_b8(nl.bf->qscale, blk, 0, 0);
     w.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        nl.bf->dscale, nl.wlive ? 4 * (blk >> 8) : 0xFFFFFFF0u, 0, 0));
+                                        nl.bf->dscale, nl.wlive ? 4 * (blk >> nl.bf->dshift) : 0xFFFFFFF0u,
+                                        0, 0));
   }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -499,8 +500,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   const int wsrc = DUAL ? (__builtin_amdgcn_readfirstlane(wave) & 1) : 0;
   const NF4View& wv = wsrc ? p.w2 : p.w;
   bf.codes = rsrc(wv.codes, (uint32_t)(wv.N * wv.K / 2));
-  bf.qscale = rsrc(wv.qscale, (uint32_t)(wv.N * wv.K / 64));
-  bf.dscale = rsrc(wv.dscale, (uint32_t)(4 * ((wv.N * wv.K / 64 + 255) / 256)));
+  bf.qscale = rsrc(wv.qscale, wv.fp32_scale ? 0u : (uint32_t)(wv.N * wv.K / 64));
+  bf.dscale = rsrc(wv.dscale, (uint32_t)(4 * (wv.fp32_scale ? wv.N * wv.K / 64
+                                                             : (wv.N * wv.K / 64 + 255) / 256)));
+  bf.qor = wv.fp32_scale ? 0x38u : 0u;   // E4M3 code of 1.0
+  bf.dshift = wv.fp32_scale ? 0u : 8u;
+  float lv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lv[i] = wv.lv[i];
   const uint32_t K = (uint32_t)p.w.K;
   // rows past M give offsets past the end (the host checks 32-bit room)
   const uint32_t a_base = (uint32_t)((m0 + tid / 8) * p.lda * 2) + 2 * 8 * (tid % 8);
@@ -526,7 +533,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   load_a(ra, bf, a_base, a_step, 0);
   load_w(w0, bf, w_n(0), w_k(0), whalf, K, true);
   store_a(ra, sA[0], tid);
-  store_w(w0, wdst0);
+  store_w(w0, lv, bf.qor, wdst0);
   load_a(ra, bf, a_base, a_step, BK);
   load_w(w1, bf, w_n(1), w_k(1), whalf, K, 1 < nk);
   load_w(w0, bf, w_n(2), w_k(2), whalf, K, 2 < nk);
@@ -539,14 +546,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
     {
       const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 2) * BK), w_n(kt + 3), w_k(kt + 3), whalf, K,
                          kt + 3 < nk};
-      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl);
+      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl, lv);
     }
     __syncthreads();
     // buffer 1 holds stage kt+1; ra = A(kt+2), w0 = W(kt+2), w1 = W(kt+3)
     {
       const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 3) * BK), w_n(kt + 4), w_k(kt + 4), whalf, K,
                          kt + 4 < nk};
-      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl);
+      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl, lv);
     }
     __syncthreads();
   }
@@ -641,7 +648,7 @@ static hipError_t launch(const BigArgs& p, hipStream_t st) {
 static bool fits_32bit(int64_t M, int64_t lda, const NF4View& w) {
   const int64_t lim = (int64_t)1 << 31;
   return (M + big::BM) * lda * 2 + 8 * big::BK * 2 < lim && (w.N + big::BN) * w.K / 2 < lim &&
-         w.N * w.K / 64 < lim;
+         w.N * w.K / 64 < lim && 4 * scale_d_count(w) < lim;
 }
 
 hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const float* T,
@@ -666,7 +673,9 @@ hipError_t launch_fwd_dual(const NF4View& wg, const NF4View& wu, const u16* X, i
                            float s, int epilogue, u16* Yg, u16* Yu, hipStream_t st) {
   const int64_t N = wg.N, K = wg.K;
   const int64_t lim = (int64_t)1 << 31;
-  if ((N + big::BN) * K / 2 >= lim || N * K / 64 >= lim) return hipErrorInvalidValue;
+  if ((N + big::BN) * K / 2 >= lim || N * K / 64 >= lim || 4 * scale_d_count(wg) >= lim ||
+      4 * scale_d_count(wu) >= lim)
+    return hipErrorInvalidValue;
   int64_t mstep = (lim - 8 * big::BK * 2) / (K * 2) - big::BM;
   mstep = mstep / big::BM * big::BM;
   if (mstep < big::BM) return hipErrorInvalidValue;

@@ -44,6 +44,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 struct MergeArgs {
   const uint8_t* codes; const uint8_t* qscale; const float* dscale;   // merge: the NF4 base
+  bool fp32_scale; float lv[16];                                      // its scale format, codebook
   const u16* w_in;                                                    // unmerge: the bf16 base
   int64_t N, K;
   const u16* A; const u16* B; int r; float s;                         // s already carries the sign
@@ -103,8 +104,11 @@ __global__ __launch_bounds__(NTHREADS) void k_merge(MergeArgs p) {
     const auto rW = rsrc(UNMERGE ? (const void*)p.w_in : (const void*)p.codes,
                          UNMERGE ? N * K * 2u : N * K / 2u);
     const uint32_t nb = N * K / 64u;
-    const auto rQ = rsrc(p.qscale, UNMERGE ? 0u : nb);
-    const auto rD = rsrc(p.dscale, UNMERGE ? 0u : 4u * ((nb + 255u) / 256u));
+    // fp32 scales: q reads 0 from an empty buffer and is OR-ed with E4M3(1.0)
+    // below, d is the block's own scale
+    const auto rQ = rsrc(p.qscale, UNMERGE || p.fp32_scale ? 0u : nb);
+    const auto rD = rsrc(p.dscale, UNMERGE ? 0u : 4u * (p.fp32_scale ? nb : (nb + 255u) / 256u));
+    const uint32_t dshift = p.fp32_scale ? 0u : 8u;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -121,11 +125,11 @@ __global__ __launch_bounds__(NTHREADS) void k_merge(MergeArgs p) {
           const uint32_t blk = e / 64u;
           qb[h][i] = __builtin_amdgcn_raw_buffer_load_b8(rQ, live ? blk : 0x80000000u, 0, 0);
           dg[h][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                   rD, live ? 4u * (blk >> 8) : 0x80000000u, 0, 0));
+                                                   rD, live ? 4u * (blk >> dshift) : 0x80000000u, 0, 0));
         }
       }
   }
-  if (tid < 16) levels[tid] = __uint_as_float(kNF4LevelBits[tid]);
+  if (tid < 16) levels[tid] = p.lv[tid];
 
   // ---- stage B rows [n0, n0 + 128) x [0, RP) and A rows [0, RP) x [k0, k0 + 256) ----
   // (zeros past r, N and K: padded contraction terms then add exactly 0).
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(NTHREADS) void k_merge(MergeArgs p) {
         }
       } else {
         // W' = bf16(L[code] * fl32(E4M3(q) * d)), element e in nibble e
-        const float sb = e4m3_decode(qb[h][i] & 127u) * dg[h][i];
+        const float sb = e4m3_decode((qb[h][i] | (p.fp32_scale ? 0x38u : 0u)) & 127u) * dg[h][i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) base[e] = bf16_to_f32(f32_to_bf16(levels[(cw[h][i] >> (4 * e)) & 15u] * sb));
       }
@@ -270,6 +274,8 @@ hipError_t launch_merge(const NF4View& w, const u16* A, const u16* B, int r, flo
                         hipStream_t st) {
   mrg::MergeArgs p{};
   p.codes = w.codes; p.qscale = w.qscale; p.dscale = w.dscale;
+  p.fp32_scale = w.fp32_scale;
+  for (int i = 0; i < 16; ++i) p.lv[i] = w.lv[i];
   p.N = w.N; p.K = w.K; p.A = A; p.B = B; p.r = r; p.s = s; p.out = out;
   return mrg::launch<false>(p, st);
 }

@@ -19,26 +19,35 @@ namespace qln {
 // Host: decision points of the nearest-level rule, derived from the level
 // table by walking fp32 values around each midpoint.
 // ---------------------------------------------------------------------------
-static float level(int i) { return __builtin_bit_cast(float, kNF4LevelBits[i]); }
+static float level(const uint32_t* bits, int i) { return __builtin_bit_cast(float, bits[i]); }
 
-static bool takes_upper(float v, int j) {
-  volatile float du = level(j + 1) - v;
-  volatile float dl = v - level(j);
+static bool takes_upper(const uint32_t* bits, float v, int j) {
+  volatile float du = level(bits, j + 1) - v;
+  volatile float dl = v - level(bits, j);
   return std::fabs(du) < std::fabs(dl);  // a tie keeps the lower code
 }
 
-const EncodeCuts& encode_cuts() {
-  static EncodeCuts cuts;
+static EncodeCuts make_cuts(const uint32_t* bits) {
+  EncodeCuts cuts;
+  for (int j = 0; j < 15; ++j) {
+    float v = (float)(((double)level(bits, j) + (double)level(bits, j + 1)) * 0.5);
+    while (takes_upper(bits, std::nextafterf(v, -2.0f), j)) v = std::nextafterf(v, -2.0f);
+    while (!takes_upper(bits, v, j)) v = std::nextafterf(v, 2.0f);
+    cuts.cut[j] = v;
+  }
+  cuts.zero_code = 0;  // the code of v = 0
+  for (int j = 0; j < 15; ++j) cuts.zero_code += cuts.cut[j] <= 0.0f ? 1 : 0;
+  return cuts;
+}
+
+const EncodeCuts& encode_cuts(int codebook) {
+  static EncodeCuts cuts[2];
   static std::once_flag once;
   std::call_once(once, [] {
-    for (int j = 0; j < 15; ++j) {
-      float v = (float)(((double)level(j) + (double)level(j + 1)) * 0.5);
-      while (takes_upper(std::nextafterf(v, -2.0f), j)) v = std::nextafterf(v, -2.0f);
-      while (!takes_upper(v, j)) v = std::nextafterf(v, 2.0f);
-      cuts.cut[j] = v;
-    }
+    cuts[CODEBOOK_NF4] = make_cuts(kNF4LevelBits);
+    cuts[CODEBOOK_INT4] = make_cuts(kINT4LevelBits);
   });
-  return cuts;
+  return cuts[codebook == CODEBOOK_INT4 ? CODEBOOK_INT4 : CODEBOOK_NF4];
 }
 
 // ---------------------------------------------------------------------------
@@ -58,7 +67,12 @@ const EncodeCuts& encode_cuts() {
 // points are >= 0.079 apart) and the count below it.  Whenever q is within
 // 2^-20 of that decision point, or the block scale is outside [2^-100, 2^100]
 // (including an all-zero block), the lane redoes its elements with an IEEE
-// division, so the result always equals code(RN(x/a)).
+// division, so the result always equals code(RN(x/a)).  The same holds for any
+// codebook whose decision points are at least 1/128 apart (NF4, INT4).
+//
+// FP32 (no double quantization, Transformers "Bitsandbytes" 4-bit section):
+// the group's exact block absmax values go to dscale[b] as fp32 and qscale is
+// not written.
 // ---------------------------------------------------------------------------
 constexpr int QBINS = 256;
 constexpr float BIN_PAD = 0x1p-12f;
@@ -75,6 +89,7 @@ __device__ __forceinline__ int bin_of(float q) {
   return min(max(b, 0), QBINS - 1);
 }
 
+template <bool FP32>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ qscale,
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
       word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        int c = 7;  // all-zero block: the exact zero level
+        int c = cuts.zero_code;  // all-zero block: the code of v = 0
         if (a > 0.0f) {
           const float q = x[e] / a;
           const BinEntry be = s_bin[bin_of(q)];
@@ -171,8 +186,12 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&s_codes[i * 8]),
                                 reinterpret_cast<u32x4_t*>(codes + b0 * 32) + i);
 
-  // double quantization of this group's block scales
   const float a_t = tid < nbg ? s_amax[tid] : 0.0f;
+  if constexpr (FP32) {  // the scales themselves, no double quantization
+    if (tid < nbg) dscale[b0 + tid] = a_t;
+    return;
+  }
+  // double quantization of this group's block scales
   const float wm = wave_max(a_t);
   if (lane == 0) s_wmax[wave] = wm;
   __syncthreads();
@@ -190,12 +209,17 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   }
 }
 
-hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
-                           uint8_t* qscale, float* dscale, float* absmax, hipStream_t s) {
+hipError_t launch_quantize(const float* W, int64_t N, int64_t K, int codebook, bool fp32_scale,
+                           uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax,
+                           hipStream_t s) {
   const int64_t nb = N * K / 64;
   const int64_t ng = (nb + 255) / 256;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
-                     dscale, absmax, encode_cuts());
+  if (fp32_scale)
+    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
+                       dscale, absmax, encode_cuts(codebook));
+  else
+    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
+                       dscale, absmax, encode_cuts(codebook));
   return hipGetLastError();
 }
 
@@ -206,40 +230,48 @@ hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
 // 8 codes of block 8j + lane/8 (one 4-byte load) and writes their 8 bf16 values
 // with one 16-byte store, so every load instruction reads 256 contiguous bytes
 // and every store instruction writes 1 KiB.  All loads are issued before any
-// arithmetic; the level table sits in LDS.
+// arithmetic; the level table (the weight's codebook) sits in LDS.  FP32: the
+// block scale is dscale[b] itself.
 // ---------------------------------------------------------------------------
 constexpr int DQ_STEPS = 8;  // 8 blocks per wave and step
 
+struct Levels { float v[16]; };
+
+template <bool FP32>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ qscale,
                                                     const float* __restrict__ dscale,
-                                                    int64_t nblocks, u16* __restrict__ out) {
+                                                    int64_t nblocks, u16* __restrict__ out,
+                                                    Levels lv) {
   __shared__ float s_L[16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t g = blockIdx.x;
   const int64_t b0 = g * 256 + wave * 64;               // first block of this wave
   const int64_t nbw = min<int64_t>(64, nblocks - b0);  // its blocks (<= 0 past the end)
-  if (tid < 16) s_L[tid] = __uint_as_float(kNF4LevelBits[tid]);
-  const float d = dscale[g];
+  if (tid < 16) s_L[tid] = lv.v[tid];
+  const float d = FP32 ? 0.0f : dscale[g];
   uint32_t c[DQ_STEPS], qv[DQ_STEPS];
+  float sv[DQ_STEPS];
 #pragma unroll
   for (int j = 0; j < DQ_STEPS; ++j) {
     const int blk = j * 8 + (lane >> 3);
     if (blk < nbw) {
       c[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + (b0 + blk) * 32) +
                                         (lane & 7));
-      qv[j] = qscale[b0 + blk];
+      if constexpr (FP32) sv[j] = dscale[b0 + blk];
+      else qv[j] = qscale[b0 + blk];
     } else {
       c[j] = 0;
       qv[j] = 0;
+      sv[j] = 0.0f;
     }
   }
   __syncthreads();  // level table ready
 #pragma unroll
   for (int j = 0; j < DQ_STEPS; ++j) {
     const int blk = j * 8 + (lane >> 3);
-    const float sc = e4m3_decode(qv[j]) * d;
+    const float sc = FP32 ? sv[j] : e4m3_decode(qv[j]) * d;
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -255,8 +287,14 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 hipError_t launch_dequantize(const NF4View& w, u16* out, hipStream_t s) {
   const int64_t nb = w.N * w.K / 64;
   const int64_t ng = (nb + 255) / 256;
-  hipLaunchKernelGGL(k_dequantize, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
-                     w.dscale, nb, out);
+  Levels lv;
+  for (int i = 0; i < 16; ++i) lv.v[i] = w.lv[i];
+  if (w.fp32_scale)
+    hipLaunchKernelGGL(k_dequantize<true>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
+                       w.dscale, nb, out, lv);
+  else
+    hipLaunchKernelGGL(k_dequantize<false>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
+                       w.dscale, nb, out, lv);
   return hipGetLastError();
 }
 

@@ -54,13 +54,13 @@
 extern "C" {
 #endif
 
-#define QLORA_ABI_VERSION 1
+#define QLORA_ABI_VERSION 2
 
 typedef enum {
   QL_OK = 0,
   QL_ERR_NULL = -1,         /* a required pointer is NULL                          */
   QL_ERR_SHAPE = -2,        /* a size is non-positive, or cols % 64 != 0           */
-  QL_ERR_UNSUPPORTED = -3,  /* block != 64, dq_block != 256, dtype != bf16, r range */
+  QL_ERR_UNSUPPORTED = -3,  /* block, dq_block, codebook, dtype or r out of range  */
   QL_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned             */
   QL_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required          */
   QL_ERR_HIP = -6           /* the HIP runtime reported an error at launch         */
@@ -70,22 +70,34 @@ enum { QL_DTYPE_BF16 = 1 };  /* the only compute dtype: bfloat16 operands, fp32 
 
 #define QLORA_MAX_RANK 128
 
+/* Codebooks: the 16 levels a 4-bit code indexes (qlora_codebook_levels()).
+ * NF4 is the QLoRA data type; INT4 is the evenly spaced comparison codebook
+ * of the Ultralytics "QLoRA" encoding snippet. */
+enum { QL_CODEBOOK_NF4 = 0, QL_CODEBOOK_INT4 = 1 };
+
 /* A quantized frozen weight W [rows = N][cols = K] (device pointers).
  *  codes  : N*K/2 bytes; byte e/2 holds flattened element e, even e in the low
- *           nibble; the code indexes the 16 NF4 levels (nf4_levels()).
- *  qscale : nb = N*K/64 bytes; OCP FP8 E4M3 code of each block's scale
- *           (block b covers flattened elements [64b, 64b+64), always inside
- *           one row because K % 64 == 0).
- *  dscale : ng = ceil(nb/256) fp32; group g covers blocks [256g, 256g+256)
- *           (the last group may be shorter); restored block scale is
- *           fl32(E4M3(qscale[b]) * dscale[b/256]).
- *  block, dq_block: must be 64 and 256. */
+ *           nibble; the code indexes the 16 levels of `codebook`.
+ *  block  : must be 64 (block b covers flattened elements [64b, 64b+64),
+ *           always inside one row because K % 64 == 0); nb = N*K/64.
+ *  dq_block = 256 (double quantization, the QLoRA default):
+ *    qscale : nb bytes, OCP FP8 E4M3 code of each block's scale;
+ *    dscale : ng = ceil(nb/256) fp32; group g covers blocks [256g, 256g+256)
+ *             (the last may be shorter); restored block scale is
+ *             fl32(E4M3(qscale[b]) * dscale[b/256]).
+ *  dq_block = 0 (no double quantization; Transformers "Bitsandbytes", 4-bit
+ *    section, nested quantization off):
+ *    qscale : unused, may be NULL;
+ *    dscale : nb fp32, the block scales (each block's exact absmax).
+ *  codebook: QL_CODEBOOK_NF4 (0, the default of a zero-initialised
+ *    descriptor) or QL_CODEBOOK_INT4. */
 typedef struct {
   const uint8_t* codes;
   const uint8_t* qscale;
   const float* dscale;
   int64_t rows, cols;
   int32_t block, dq_block;
+  int32_t codebook;
 } qlora_nf4_weight;
 
 /* ABI version (QLORA_ABI_VERSION of the built library). */
@@ -102,8 +114,14 @@ const char* qlora_last_error(void);
  * largest, each rounded once to fp32.  Code 0 is -1, code 7 is +0, code 15 is +1. */
 void nf4_levels(float out[16]);
 
+/* The 16 levels of a codebook in code order (host memory, 16 floats): NF4 as
+ * nf4_levels(); INT4 is L[i] = -1 + 2 i / 15 rounded once to fp32 (no zero
+ * level).  Returns QL_OK, QL_ERR_UNSUPPORTED or QL_ERR_NULL. */
+int qlora_codebook_levels(int codebook, float out[16]);
+
 /* Storage of a quantized [rows][cols] weight (host outputs, any may be NULL):
- * codes rows*cols/2 bytes, qscale rows*cols/64 bytes, dscale 4*ceil(nb/256)
+ * codes rows*cols/2 bytes; with dq_block 256, qscale rows*cols/64 bytes and
+ * dscale 4*ceil(nb/256) bytes; with dq_block 0, qscale 0 and dscale 4*nb
  * bytes.  Returns QL_OK or QL_ERR_SHAPE / QL_ERR_UNSUPPORTED. */
 int nf4_storage_bytes(int64_t rows, int64_t cols, int block, int dq_block,
                       size_t* codes_bytes, size_t* qscale_bytes, size_t* dscale_bytes);
@@ -117,13 +135,25 @@ int nf4_storage_bytes(int64_t rows, int64_t cols, int block, int dq_block,
  *   d_g   = fl32(max_{b in g} a_b / 448)                       -> dscale[g]
  *   q_b   = E4M3_RNE(fl32(a_b / d_g)), 0 when d_g == 0           -> qscale[b]
  * Outputs: codes [rows*cols/2], qscale [nb], dscale [ng] (device);
- * absmax_out [nb] fp32 (device, may be NULL) receives the exact a_b. */
+ * absmax_out [nb] fp32 (device, may be NULL) receives the exact a_b.
+ * dq_block 0 skips the double quantization: dscale [nb] receives a_b and
+ * qscale may be NULL (as qlora_quantize with QL_CODEBOOK_NF4). */
 int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_block,
                  uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
                  void* stream);
 
+/* Quantize with a codebook (QL_CODEBOOK_NF4 or QL_CODEBOOK_INT4) and a scale
+ * format (dq_block 256: double-quantized E4M3 scales; 0: fp32 block scales
+ * in dscale [nb], qscale unused).  Same rule as nf4_quantize with the
+ * codebook's levels; an all-zero block gets the code of v = 0 (the nearest
+ * level, the lower on a tie: 7 for both codebooks). */
+int qlora_quantize(const float* W, int64_t rows, int64_t cols, int codebook, int dq_block,
+                   uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
+                   void* stream);
+
 /* Dequantize to bfloat16: W_bf16[e] = bf16_RNE(fl32(L[code_e] * s_b)) with the
- * restored block scale s_b = fl32(E4M3(q_b) * d_g).  Transformers docs
+ * restored block scale s_b = fl32(E4M3(q_b) * d_g) (or the fp32 dscale[b]
+ * when dq_block is 0) and L the weight's codebook.  Transformers docs
  * "Bitsandbytes", section on dequantizing a model to its original precision;
  * Ultralytics "QLoRA" (restore = level times block scale).
  * W_bf16: device, rows*cols uint16 (bf16 bits). */
@@ -138,7 +168,8 @@ size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
  *   Y[m][n]      = bf16(sum_k X[m][k] W'[n][k] + s sum_j T[m][j] B[n][j])  [M][N]
  * with s = fl32(alpha / r); products of bf16 operands summed in fp32 (MFMA).
  * For M > 16 T enters the LoRA product as bf16(s T); for M <= 16 with K a
- * multiple of 256 (the HBM-bound decode path) the LoRA sum is fp32 and each
+ * multiple of 256 and double-quantized scales (the HBM-bound decode path)
+ * the LoRA sum is fp32 and each
  * 64-block's partial dot product with bf16(L[code]) is scaled by the block
  * scale in fp32, which rounds the weight's relative value to bf16 once, as
  * dequantization does (other shapes take the M > 16 path).

@@ -33,7 +33,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"nf4_quantize", "nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"missing export {n}"
-    assert q.qlora_abi_version() == 1
+    header = open(os.path.join(ROOT, "include", "qlora_nf4.h")).read()
+    assert q.qlora_abi_version() == int(re.search(r"#define QLORA_ABI_VERSION (\d+)", header).group(1))
 
 
 def test_levels_match_oracle_bitwise(orc):
@@ -191,3 +192,29 @@ def test_dual_rejects_bad_arguments():
     assert _dual(wg, wu, epi=2, H=FAKE + 2) == -4
     assert _dual(wg, wu, M=4096, ws=None, wsb=0) == -5   # the rank-r product needs a workspace
     assert q.lib().qlora_last_error() != b""
+
+
+def test_codebooks_and_scale_formats_are_validated():
+    """Codebook and dq_block are checked before any launch; fp32 block scales
+    (dq_block 0) need no qscale buffer; the levels and storage sizes follow the
+    header."""
+    L = q.lib()
+    w = _weight()
+    w.codebook = 2
+    assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == -3
+    w = _weight(dq=128)
+    assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == -3
+    w = _weight(dq=256, qs=None)
+    assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == -1
+    w = _weight(dq=0, qs=None)
+    assert L.nf4_dequantize(ctypes.byref(w), FAKE + 4, None) == -4     # got past the weight checks
+    assert L.qlora_quantize(FAKE, 64, 64, 3, 256, FAKE, FAKE, FAKE, None, None) == -3
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 64, FAKE, FAKE, FAKE, None, None) == -3
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 256, FAKE, None, FAKE, None, None) == -1
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 0, FAKE, None, FAKE + 4, None, None) == -4
+    assert q.nf4_storage_bytes(128, 256, 64, 0) == (128 * 256 // 2, 0, 4 * 128 * 256 // 64)
+    assert q.nf4_storage_bytes(128, 256, 64, 256) == (128 * 256 // 2, 512, 4 * 2)
+    lv = q.codebook_levels("int4")
+    assert lv[0] == -1.0 and lv[15] == 1.0 and all(a < b for a, b in zip(lv, lv[1:]))
+    assert q.codebook_levels("nf4") == q.nf4_levels()
+    assert ctypes.sizeof(q._Weight) == 56
