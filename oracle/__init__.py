@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_lora_merge.restype = I
         L.oracle_swiglu.argtypes = [P, P, I64, P]
         L.oracle_swiglu.restype = None
+        L.oracle_adamw_step.argtypes = [P, P, P, P, I64, D, D, D, D, D, I]
+        L.oracle_adamw_step.restype = None
         _lib = L
     return _lib
 
@@ -312,3 +314,17 @@ def swiglu(G, U):
     h = np.empty_like(g)
     lib().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
     return h
+
+
+
+def adamw_step(theta, m, v, g, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+               weight_decay: float = 0.0, step: int = 1):
+    """One AdamW step in double; returns (theta, m, v) as new float64 arrays."""
+    th = np.array(theta, dtype=np.float64, copy=True).ravel()
+    mm = np.array(m, dtype=np.float64, copy=True).ravel()
+    vv = np.array(v, dtype=np.float64, copy=True).ravel()
+    gg = np.ascontiguousarray(g, dtype=np.float64).ravel()
+    assert th.size == mm.size == vv.size == gg.size and step >= 1
+    lib().oracle_adamw_step(_ptr(th), _ptr(mm), _ptr(vv), _ptr(gg), th.size, float(lr), float(beta1),
+                            float(beta2), float(eps), float(weight_decay), int(step))
+    return th, mm, vv

@@ -621,3 +621,20 @@ void oracle_swiglu(const double* G, const double* U, int64_t n, double* H) {
     H[i] = g / (1.0 + exp(-g)) * U[i];
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Adapter optimizer step: Adam with bias correction and decoupled weight   */
+/* decay (the state that the paged optimizers of the pages hold).            */
+/* ------------------------------------------------------------------------ */
+void oracle_adamw_step(double* theta, double* m, double* v, const double* g, int64_t n, double lr,
+                       double b1, double b2, double eps, double wd, int t) {
+  const double bc1 = 1.0 - pow(b1, (double)t);
+  const double bc2 = 1.0 - pow(b2, (double)t);
+  for (int64_t i = 0; i < n; ++i) {
+    double th = theta[i] * (1.0 - lr * wd);
+    m[i] = b1 * m[i] + (1.0 - b1) * g[i];
+    v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
+    th -= lr * (m[i] / bc1) / (sqrt(v[i] / bc2) + eps);
+    theta[i] = th;
+  }
+}

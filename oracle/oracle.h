@@ -155,6 +155,18 @@ int oracle_lora_merge(const uint16_t* W_base, int64_t N, int64_t K, const uint16
  * outputs (each a qlora forward); H may equal G or U. */
 void oracle_swiglu(const double* G, const double* U, int64_t n, double* H);
 
+/* One optimizer step of the adapters (Ultralytics "QLoRA", "How QLoRA works",
+ * paged-optimizer bullet, and vnread "Grokking QLoRA", "Paged Optimizers":
+ * Adam keeps a momentum and a variance per parameter, the state QLoRA pages
+ * out under memory pressure).  The pages do not write the update out; this is
+ * Adam (bias-corrected moments) with decoupled weight decay, AdamW, in double:
+ *   theta <- theta (1 - lr wd)
+ *   m     <- b1 m + (1 - b1) g,      v <- b2 v + (1 - b2) g^2
+ *   theta <- theta - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ * t >= 1 is the step number.  theta, m, v are updated in place. */
+void oracle_adamw_step(double* theta, double* m, double* v, const double* g, int64_t n, double lr,
+                       double b1, double b2, double eps, double wd, int t);
+
 #ifdef __cplusplus
 }
 #endif

@@ -626,3 +626,51 @@ def test_variant_dequant_error_bound_and_self_codes(orc, codebook, dq):
         got = orc.dequantize(c2, q2, d2, 1, 64, codebook=codebook)
         want = torch.from_numpy(blk).bfloat16().view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got, want), (codebook, dq, e)
+
+
+# --------------------------------------------------------------------------
+# Adapter optimizer step (AdamW)
+# --------------------------------------------------------------------------
+def test_adamw_closed_forms(orc):
+    """First step from zero state moves by lr g / (|g| + eps) after the decay;
+    a constant gradient keeps the bias-corrected moments at g and g^2, so t
+    steps move by t lr g / (|g| + eps); with g = 0 only the decay acts,
+    theta (1 - lr wd)^t."""
+    rng = np.random.default_rng(31)
+    n = 257
+    th0 = rng.normal(size=n)
+    g = rng.normal(size=n) * 10.0 ** rng.integers(-4, 2, n)
+    lr, wd, eps = 1e-3, 0.05, 1e-8
+    th, m, v = orc.adamw_step(th0, np.zeros(n), np.zeros(n), g, lr, weight_decay=wd, eps=eps)
+    assert np.allclose(th, th0 * (1 - lr * wd) - lr * g / (np.abs(g) + eps), rtol=0, atol=1e-15)
+    assert np.allclose(m, 0.1 * g, rtol=1e-15) and np.allclose(v, 0.001 * g * g, rtol=1e-12)
+    th, m, v = th0.copy(), np.zeros(n), np.zeros(n)
+    for t in range(1, 8):
+        th, m, v = orc.adamw_step(th, m, v, g, lr, step=t, eps=eps)
+    assert np.allclose(th, th0 - 7 * lr * g / (np.abs(g) + eps), rtol=0, atol=1e-13)
+    th, m, v = th0.copy(), np.zeros(n), np.zeros(n)
+    for t in range(1, 6):
+        th, m, v = orc.adamw_step(th, m, v, np.zeros(n), lr, weight_decay=wd, step=t)
+    assert np.allclose(th, th0 * (1 - lr * wd) ** 5, rtol=1e-14, atol=0)
+
+
+def test_adamw_matches_torch_in_float64(orc):
+    """Five steps against torch.optim.AdamW (an independent implementation) in
+    float64, with weight decay and non-default betas."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(32)
+    n = 300
+    th0 = rng.normal(size=n)
+    grads = [rng.normal(size=n) for _ in range(5)]
+    p = torch.nn.Parameter(torch.tensor(th0, dtype=torch.float64))
+    opt = torch.optim.AdamW([p], lr=2e-3, betas=(0.8, 0.95), eps=1e-6, weight_decay=0.1)
+    th, m, v = th0.copy(), np.zeros(n), np.zeros(n)
+    for t, gr in enumerate(grads, start=1):
+        p.grad = torch.tensor(gr, dtype=torch.float64)
+        opt.step()
+        th, m, v = orc.adamw_step(th, m, v, gr, 2e-3, beta1=0.8, beta2=0.95, eps=1e-6,
+                                  weight_decay=0.1, step=t)
+        assert np.allclose(th, p.detach().numpy(), rtol=1e-13, atol=1e-15), t
+    st = opt.state[p]
+    assert np.allclose(m, st["exp_avg"].numpy(), rtol=1e-13)
+    assert np.allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-13)
