@@ -350,6 +350,53 @@ def bench_formats(hip, lay, reps=10):
     return res
 
 
+def bench_adamw(hip, layers, reps=20):
+    """AdamW step over the step's four adapter tensors (A and B of the up and
+    down projections, r=64: 4.72M parameters), without and with fp32 master
+    copies.  Algorithmic bytes per parameter: 22 (bf16 param and grad read,
+    fp32 moments read and written, bf16 param written), 30 with a master.
+    Copies of the state are rotated so that the 256 MB Infinity Cache cannot
+    hold what one step reads."""
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    st = torch.cuda.current_stream().cuda_stream
+    shapes = [tuple(t.shape) for lay in layers for t in (lay.A, lay.B)]
+    nparam = sum(a * b for a, b in shapes)
+    res = {"params": nparam}
+    for master in (False, True):
+        per = 30 if master else 22
+        ncopy = max(2, -(-512 * 2**20 // (per * nparam)))
+        sets = []
+        for c in range(ncopy):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(100 + c)
+            ps = [(torch.randn(sh, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for sh in shapes]
+            gs = [(torch.randn(sh, generator=g, device="cuda") * 1e-3).to(torch.bfloat16) for sh in shapes]
+            ms = [torch.zeros(sh, device="cuda") for sh in shapes]
+            vs = [torch.zeros(sh, device="cuda") for sh in shapes]
+            ws = [p.float() for p in ps] if master else None
+            sets.append((ps, gs, ms, vs, ws))
+
+        def one(i):
+            ps, gs, ms, vs, ws = sets[i % ncopy]
+            q.qlora_adamw_step(ps, gs, ms, vs, 1e-4, weight_decay=0.01, step=i + 1, masters=ws)
+        for i in range(3):
+            one(i)
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for i in range(reps):
+            one(i)
+        hip.record(e1, st)
+        ms_step = hip.elapsed_ms(e0, e1) / reps
+        gbs = per * nparam / (ms_step * 1e-3) / 1e9
+        res["master" if master else "no_master"] = {"us_per_step": round(ms_step * 1e3, 1), "GB/s": round(gbs, 1),
+                                                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_library_reference(hip, layers, reps=10):
     """Context only, not part of the path: a dense bf16 matmul from the vendor
     library (torch -> hipBLASLt) on the same shapes as the two fused forward
@@ -561,6 +608,8 @@ def main():
         extras["dual"] = bench_dual(hip, up)
         log("[bench] codebook and scale-format variants")
         extras["formats"] = bench_formats(hip, up)
+        log("[bench] adapter AdamW step")
+        extras["adamw"] = bench_adamw(hip, layers)
         log("[bench] library reference")
         extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
 

@@ -39,6 +39,11 @@ class QLoRAError(RuntimeError):
         self.status = status
 
 
+class _AdamwTensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("master", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
 class _Weight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
                 ("dscale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
@@ -74,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd.restype = I
     L.qlora_dual_fwd.argtypes = [WP, WP, P, I64, P, P, P, P, I, F, I, I, P, P, P, P, P, P, SZ, P]
     L.qlora_dual_fwd.restype = I
+    L.qlora_adamw_step.argtypes = [P, I, F, F, F, F, F, I, P]
+    L.qlora_adamw_step.restype = I
     L.qlora_bwd_workspace_bytes.argtypes = [I64, I64, I64, I]
     L.qlora_bwd_workspace_bytes.restype = SZ
     L.qlora_linear_bwd.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P, SZ, P]
@@ -306,6 +313,32 @@ def qlora_dual_fwd(w_gate: NF4Weight, w_up: NF4Weight, X, A_gate, B_gate, A_up, 
                                 _ptr(Yg), _ptr(Yu), _ptr(H), Tg.data_ptr(), Tu.data_ptr(), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(stream)))
     return (H, Tg, Tu) if swiglu else (Yg, Yu, Tg, Tu)
+
+
+def qlora_adamw_step(params, grads, exp_avgs, exp_avg_sqs, lr: float, betas=(0.9, 0.999),
+                     eps: float = 1e-8, weight_decay: float = 0.0, step: int = 1, masters=None,
+                     stream=None) -> None:
+    """One AdamW step over lists of tensors, in place: bf16 params (cuda),
+    bf16 grads, fp32 moments, optional fp32 master copies (a list with None
+    entries allowed)."""
+    import torch
+    n = len(params)
+    masters = masters if masters is not None else [None] * n
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == len(masters) == n):
+        raise ValueError("tensor lists differ in length")
+    arr = (_AdamwTensor * max(1, n))()
+    for i, (p, g, m, v, w) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs, masters)):
+        shape = tuple(p.shape)
+        _need(p, torch.bfloat16, shape, f"params[{i}]")
+        _need(g, torch.bfloat16, shape, f"grads[{i}]")
+        _need(m, torch.float32, shape, f"exp_avgs[{i}]")
+        _need(v, torch.float32, shape, f"exp_avg_sqs[{i}]")
+        if w is not None:
+            _need(w, torch.float32, shape, f"masters[{i}]")
+        arr[i] = _AdamwTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), _ptr(w), p.numel())
+    _check(lib().qlora_adamw_step(ctypes.cast(arr, ctypes.c_void_p), n, float(lr), float(betas[0]),
+                                  float(betas[1]), float(eps), float(weight_decay), int(step),
+                                  _stream(stream)))
 
 
 def qlora_linear_bwd(w: NF4Weight, X, dY, A, B, alpha: float, T=None, want_dX: bool = True,

@@ -25,6 +25,7 @@ SOURCES = {
     "gemm_big.hip": [],
     "decode.hip": [],
     "merge.hip": [],
+    "optim.hip": [],
     "capi.hip": [],
 }
 

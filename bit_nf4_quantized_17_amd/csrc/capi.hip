@@ -4,7 +4,9 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
+#include <vector>
 #include <string>
 
 #include "../../include/qlora_nf4.h"
@@ -299,6 +301,30 @@ int qlora_dual_fwd(const qlora_nf4_weight* w_gate, const qlora_nf4_weight* w_up,
                       alpha / (float)r, epilogue == QL_DUAL_SEPARATE ? 1 : 2, out1, out2, st);
   record(g_hook.fwd_end, st);
   return hip_status(e, "qlora_dual_fwd: main launch");
+}
+
+int qlora_adamw_step(const qlora_adamw_tensor* tensors, int count, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, int step, void* stream) {
+  if (count < 0) return fail(QL_ERR_SHAPE, "count=%d", count);
+  if (count > 0 && !tensors) return fail(QL_ERR_NULL, "tensor list is NULL");
+  if (step < 1) return fail(QL_ERR_UNSUPPORTED, "step=%d (counts from 1)", step);
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps >= 0.0f) ||
+      !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return fail(QL_ERR_UNSUPPORTED, "hyperparameters out of range (0 <= beta < 1, eps >= 0, finite lr, wd)");
+  std::vector<AdamwTensor> ts((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const qlora_adamw_tensor& t = tensors[i];
+    if (t.numel < 0 || t.numel >= ((int64_t)1 << 40)) return fail(QL_ERR_SHAPE, "tensor %d: numel=%lld", i, (long long)t.numel);
+    if (t.numel > 0 && (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq))
+      return fail(QL_ERR_NULL, "tensor %d: a required pointer is NULL", i);
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.exp_avg) || !aligned16(t.exp_avg_sq) ||
+        (t.master && !aligned16(t.master)))
+      return fail(QL_ERR_ALIGN, "tensor %d: device pointers must be 16-byte aligned", i);
+    ts[i] = AdamwTensor{t.param, t.grad, t.exp_avg, t.exp_avg_sq, t.master, t.numel};
+  }
+  return hip_status(launch_adamw(ts.data(), count, lr, beta1, beta2, eps, weight_decay, step,
+                                 (hipStream_t)stream),
+                    "qlora_adamw_step launch");
 }
 
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {

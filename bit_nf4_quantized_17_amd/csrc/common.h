@@ -104,6 +104,13 @@ hipError_t launch_lora_da(const float* U, const u16* X, int64_t M, int64_t K, in
 // Y = X W'^T + s T B^T
 hipError_t launch_fwd_main(const NF4View& w, const u16* X, int64_t M, const float* T,
                            const u16* B, int r, float s, u16* Y, hipStream_t st);
+// one AdamW tensor: bf16 parameter and gradient, fp32 moments, optional fp32 master
+struct AdamwTensor {
+  u16* param; const u16* grad; float* exp_avg; float* exp_avg_sq; float* master; int64_t n;
+};
+hipError_t launch_adamw(const AdamwTensor* ts, int count, float lr, float b1, float b2, float eps,
+                        float wd, int step, hipStream_t st);
+
 // gate and up projections of one X: Yg = X Wg'^T + s Tg Bg^T, Yu likewise;
 // epilogue 1 writes both, 2 writes bf16(silu(g) * u) into Yg (Yu unused)
 hipError_t launch_fwd_dual(const NF4View& wg, const NF4View& wu, const u16* X, int64_t M,

@@ -211,6 +211,37 @@ int qlora_dual_fwd(const qlora_nf4_weight* w_gate, const qlora_nf4_weight* w_up,
                    uint16_t* H, float* T_gate_save, float* T_up_save,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* One tensor of an optimizer step: the bf16 parameter and its gradient, the
+ * fp32 first and second moments (same element count), and an optional fp32
+ * master copy of the parameter (NULL: the bf16 parameter is the value). */
+typedef struct {
+  uint16_t* param;
+  const uint16_t* grad;
+  float* exp_avg;
+  float* exp_avg_sq;
+  float* master;
+  int64_t numel;
+} qlora_adamw_tensor;
+
+/* One AdamW step of the adapters over `count` tensors, in as few launches as
+ * the tensor list allows (24 tensors each).  Ultralytics "QLoRA", "How QLoRA
+ * works" (paged-optimizer bullet) and vnread "Grokking QLoRA", "Paged
+ * Optimizers": only the adapters train, and Adam keeps a momentum and a
+ * variance per parameter.  The update (Adam with bias correction and
+ * decoupled weight decay), in fp32 per element:
+ *   theta <- theta (1 - lr weight_decay)
+ *   m <- beta1 m + (1 - beta1) g,   v <- beta2 v + (1 - beta2) g^2
+ *   theta <- theta - (lr / (1 - beta1^step)) m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ * theta comes from master when given (which receives the new value) and from
+ * the bf16 param otherwise; param always receives bf16_RNE(theta).  The
+ * moments and master are read and written in place; grad is only read.
+ * The pointers may be any device-accessible memory, managed (unified)
+ * memory included, which the runtime may page to the host under pressure;
+ * the kernel makes no assumption about where the pages live.  step >= 1; 0 <= beta < 1; eps >= 0.  A tensor with
+ * numel 0 is skipped. */
+int qlora_adamw_step(const qlora_adamw_tensor* tensors, int count, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, int step, void* stream);
+
 /* Workspace the backward needs (bytes, 256-byte granular). */
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 

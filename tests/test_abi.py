@@ -218,3 +218,26 @@ def test_codebooks_and_scale_formats_are_validated():
     assert lv[0] == -1.0 and lv[15] == 1.0 and all(a < b for a, b in zip(lv, lv[1:]))
     assert q.codebook_levels("nf4") == q.nf4_levels()
     assert ctypes.sizeof(q._Weight) == 56
+
+
+def test_adamw_rejects_bad_arguments():
+    L = q.lib()
+    T = q._AdamwTensor
+    good = (T * 1)(T(FAKE, FAKE, FAKE, FAKE, None, 1024))
+
+    def call(arr, count=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1):
+        return L.qlora_adamw_step(ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, count,
+                                  lr, b1, b2, eps, wd, step, None)
+    assert call(None, count=0) == 0                      # nothing to do
+    assert call(None) == -1
+    assert call(good, count=-1) == -2
+    assert call(good, step=0) == -3
+    assert call(good, b1=1.0) == -3
+    assert call(good, b2=-0.1) == -3
+    assert call(good, eps=-1.0) == -3
+    assert call(good, lr=float("nan")) == -3
+    assert call((T * 1)(T(FAKE, None, FAKE, FAKE, None, 8))) == -1
+    assert call((T * 1)(T(FAKE, FAKE, FAKE, FAKE, None, -1))) == -2
+    assert call((T * 1)(T(FAKE, FAKE, FAKE + 4, FAKE, None, 8))) == -4
+    assert call((T * 1)(T(FAKE, FAKE, FAKE, FAKE, FAKE + 8, 8))) == -4
+    assert call((T * 1)(T(None, None, None, None, None, 0))) != -1   # empty tensors need no buffers
