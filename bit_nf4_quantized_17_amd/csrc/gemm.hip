@@ -35,7 +35,10 @@ constexpr int BK = 64;
 constexpr int PITCH = BK + 8;  // bf16 elements per LDS row (144 bytes)
 constexpr int NTHREADS = 256;
 
-enum { SRC_CC = 0, SRC_T = 1, SRC_NF4CC = 2, SRC_NF4T = 3, SRC_TF32S = 4 };
+enum { SRC_CC = 0, SRC_T = 1, SRC_NF4CC = 2, SRC_NF4T = 3, SRC_TF32S = 4,
+       SRC_TR = 5,      // A from a [C][I] matrix, kept [c][i] in LDS, read with transposing loads
+       SRC_TF32SR = 6   // B from an fp32 [C][J] matrix as hi + lo bf16, kept [c][j], transposing loads
+};
 enum { LORA_NONE = 0, LORA_FWD = 1, LORA_DX = 2 };
 enum { OUT_BF16 = 0, OUT_F32 = 1 };
 
@@ -112,6 +115,98 @@ struct ProdT {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         S[(iseg + e) * PITCH + lane] = (u16)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+};
+
+// Tiles of a matrix whose contiguous dimension is the output index (dY or X
+// for dB and dA): loaded with whole 256-byte row segments (16 lanes per
+// contraction row) and kept in LDS as [64 c][R + 8] rows, so both the global
+// loads and the 16-byte LDS stores are contiguous; the MFMA fragments come out
+// with the transposing LDS read (ds_read_b64_tr_b16).
+template <int R>
+constexpr int tr_pitch() { return R + 8; }
+
+typedef __attribute__((address_space(3))) short lds_short_g;
+typedef short s16x4_g __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_g lds_s16x4_g;
+
+// MFMA operand fragment of column block cb (32 columns) at contraction step ks
+// from a [c][cols] bf16 tile: lane l receives 8 contraction values of column
+// cb*32 + l%32 (within each 16-lane group, lane i gets element i%4 of the rows
+// addressed by lanes 4j + i/4).
+__device__ __forceinline__ bf16x8_t read_tr(const u16* S, int pitch, int col0, int ks, int lane) {
+  const int L = lane & 15;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+  const int row = ks * 16 + 8 * (lane >> 5) + (L >> 2);
+  const lds_short_g* base = (const lds_short_g*)S;
+  const s16x4_g lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_g*)(base + row * pitch + col));
+  const s16x4_g hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_g*)(base + (row + 4) * pitch + col));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// bf16 [C][cols] source, R = 128 output columns: thread t loads row
+// c0 + t/16 + 16q (q < 4), columns i0 + 8 (t % 16) .. +8
+template <int R>
+struct ProdTR {
+  static_assert(R == 128, "16 lanes x 8 columns per row");
+  uint4 v[4];
+  __device__ void load(const u16* src, int64_t ld, int64_t C, int64_t cols, int64_t i0,
+                       int64_t c0, bool vec, int tid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = load8_guarded(src, c0 + tid / 16 + 16 * q, C, ld, i0 + (tid % 16) * 8, cols, vec);
+  }
+  __device__ void store(u16* S, int tid) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(S + (tid / 16 + 16 * q) * tr_pitch<R>() + (tid % 16) * 8) = v[q];
+  }
+};
+
+// fp32 [C][cols] source, R (32, 64 or 128) output columns, split into hi =
+// bf16(x) and lo = bf16(x - hi): thread t loads row c0 + t/16 + 16q (q < 4),
+// R/16 consecutive columns
+template <int R>
+struct ProdTF32SR {
+  static constexpr int E = R / 16;
+  float x[4][E];
+  __device__ void load(const float* src, int64_t ld, int64_t C, int64_t cols, int64_t j0,
+                       int64_t c0, bool vec, int tid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t c = c0 + tid / 16 + 16 * q, j = j0 + (tid % 16) * E;
+      if (vec && c < C && j + E <= cols) {
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          const float2 f = *reinterpret_cast<const float2*>(src + c * ld + j + e);
+          x[q][e] = f.x;
+          x[q][e + 1] = f.y;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[q][e] = (c < C && j + e < cols) ? src[c * ld + j + e] : 0.0f;
+      }
+    }
+  }
+  __device__ void store(u16* Shi, u16* Slo, int tid) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t hi[E / 2], lo[E / 2];
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        const float h0 = bf16_to_f32(f32_to_bf16(x[q][e])), h1 = bf16_to_f32(f32_to_bf16(x[q][e + 1]));
+        hi[e / 2] = pack_bf16x2(h0, h1);
+        lo[e / 2] = pack_bf16x2(x[q][e] - h0, x[q][e + 1] - h1);
+      }
+      const int off = (tid / 16 + 16 * q) * tr_pitch<R>() + (tid % 16) * E;
+#pragma unroll
+      for (int e = 0; e < E / 2; ++e) {
+        *reinterpret_cast<uint32_t*>(Shi + off + 2 * e) = hi[e];
+        *reinterpret_cast<uint32_t*>(Slo + off + 2 * e) = lo[e];
+      }
     }
   }
 };
@@ -269,10 +364,12 @@ template <int BM, int BN, int WM, int WN, int ASRC, int BSRC, int LORA, int OUT,
 __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
   static_assert(WM * WN == 4, "four waves");
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  __shared__ __attribute__((aligned(16))) u16 sA[BM * PITCH];
-  __shared__ __attribute__((aligned(16))) u16 sB[BN * PITCH];
-  constexpr bool SPLIT = (BSRC == SRC_TF32S);
-  __shared__ __attribute__((aligned(16))) u16 sB2[SPLIT ? BN * PITCH : 8];
+  constexpr int SA_E = ASRC == SRC_TR ? BK * (BM + 8) : BM * PITCH;
+  constexpr int SB_E = BSRC == SRC_TF32SR ? BK * (BN + 8) : BN * PITCH;
+  __shared__ __attribute__((aligned(16))) u16 sA[SA_E];
+  __shared__ __attribute__((aligned(16))) u16 sB[SB_E];
+  constexpr bool SPLIT = (BSRC == SRC_TF32S || BSRC == SRC_TF32SR);
+  __shared__ __attribute__((aligned(16))) u16 sB2[SPLIT ? SB_E : 8];
   __shared__ float sL[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -297,13 +394,21 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8_t fa[TM], fb[TN];
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
-        fa[a] = *reinterpret_cast<const bf16x8_t*>(
-            sA + (wm * (BM / WM) + a * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
+      for (int a = 0; a < TM; ++a) {
+        if constexpr (ASRC == SRC_TR)
+          fa[a] = read_tr(sA, BM + 8, wm * (BM / WM) + a * 32, ks, lane);
+        else
+          fa[a] = *reinterpret_cast<const bf16x8_t*>(
+              sA + (wm * (BM / WM) + a * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
+      }
 #pragma unroll
-      for (int b = 0; b < TN; ++b)
-        fb[b] = *reinterpret_cast<const bf16x8_t*>(
-            sB + (wn * (BN / WN) + b * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
+      for (int b = 0; b < TN; ++b) {
+        if constexpr (BSRC == SRC_TF32SR)
+          fb[b] = read_tr(sB, BN + 8, wn * (BN / WN) + b * 32, ks, lane);
+        else
+          fb[b] = *reinterpret_cast<const bf16x8_t*>(
+              sB + (wn * (BN / WN) + b * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
+      }
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -311,9 +416,13 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
       if constexpr (SPLIT) {
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
-          fb[b] = *reinterpret_cast<const bf16x8_t*>(
-              sB2 + (wn * (BN / WN) + b * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
+        for (int b = 0; b < TN; ++b) {
+          if constexpr (BSRC == SRC_TF32SR)
+            fb[b] = read_tr(sB2, BN + 8, wn * (BN / WN) + b * 32, ks, lane);
+          else
+            fb[b] = *reinterpret_cast<const bf16x8_t*>(
+                sB2 + (wn * (BN / WN) + b * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8);
+        }
 #pragma unroll
         for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -353,11 +462,14 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
   }
 
   // ---- main contraction ----
-  using PA = typename std::conditional<ASRC == SRC_CC, ProdCC<BM>, ProdT<BM>>::type;
+  using PA = typename std::conditional<
+      ASRC == SRC_CC, ProdCC<BM>,
+      typename std::conditional<ASRC == SRC_TR, ProdTR<BM>, ProdT<BM>>::type>::type;
   PA pa;
   ProdCC<BN> pbcc;
   ProdT<BN> pbt;
   ProdTF32S<BN> pbs;
+  ProdTF32SR<BN> pbr;
   ProdNF4CC pn;
   ProdNF4T pnt;
   const u16* bsrc = reinterpret_cast<const u16*>(p.b);
@@ -369,6 +481,8 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
     else if constexpr (BSRC == SRC_T) pbt.load(bsrc, p.ldb, p.C, p.J, j0, c0, p.b_vec, tid);
     else if constexpr (BSRC == SRC_TF32S)
       pbs.load(reinterpret_cast<const float*>(p.b), p.ldb, p.C, p.J, j0, c0, p.b_vec, tid);
+    else if constexpr (BSRC == SRC_TF32SR)
+      pbr.load(reinterpret_cast<const float*>(p.b), p.ldb, p.C, p.J, j0, c0, p.b_vec, tid);
     else if constexpr (BSRC == SRC_NF4CC) pn.load(p.w, j0, c0, tid);
     else pnt.load(p.w, j0, c0, tid);
   };
@@ -377,6 +491,7 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
     if constexpr (BSRC == SRC_CC) pbcc.store(sB, tid);
     else if constexpr (BSRC == SRC_T) pbt.store(sB, tid);
     else if constexpr (BSRC == SRC_TF32S) pbs.store(sB, sB2, tid);
+    else if constexpr (BSRC == SRC_TF32SR) pbr.store(sB, sB2, tid);
     else if constexpr (BSRC == SRC_NF4CC) pn.store(sB, sL, tid);
     else pnt.store(sB, sL, tid);
   };
@@ -447,10 +562,14 @@ int rank_tile(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Workgroups a skinny product aims for (two 128-row workgroups per CU):
+// doubling it shortened no product and doubled the fixed-order reduction.
+constexpr int64_t kSkinnyWorkgroups = 512;
+
 SkinnyPlan skinny_plan(int64_t I, int64_t C) {
   const int64_t tiles = cdiv(I, 128);
   const int64_t ctiles = cdiv(C, BK);
-  int64_t splits = std::max<int64_t>(1, cdiv(512, tiles));
+  int64_t splits = std::max<int64_t>(1, cdiv(kSkinnyWorkgroups, tiles));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, ctiles / 4));
   splits = std::min<int64_t>(splits, 64);
   const int64_t per = cdiv(ctiles, splits) * BK;
@@ -530,7 +649,7 @@ hipError_t launch_lora_db(const u16* dY, const float* T, int64_t M, int64_t N, i
   p.b = T; p.ldb = r; p.b_vec = vec_ok(T, r * 2);
   p.I = N; p.J = r; p.C = M;
   p.out = ws;
-  hipError_t e = launch_skinny<SRC_T, SRC_TF32S>(p, st);
+  hipError_t e = launch_skinny<SRC_TR, SRC_TF32SR>(p, st);
   if (e != hipSuccess) return e;
   return launch_reduce(ws, skinny_plan(N, M).splits, N, r, s, dB, r, false, st);
 }
@@ -543,7 +662,7 @@ hipError_t launch_lora_da(const float* U, const u16* X, int64_t M, int64_t K, in
   p.b = U; p.ldb = r; p.b_vec = vec_ok(U, r * 2);
   p.I = K; p.J = r; p.C = M;
   p.out = ws;
-  hipError_t e = launch_skinny<SRC_T, SRC_TF32S>(p, st);
+  hipError_t e = launch_skinny<SRC_TR, SRC_TF32SR>(p, st);
   if (e != hipSuccess) return e;
   return launch_reduce(ws, skinny_plan(K, M).splits, K, r, s, dA, K, true, st);
 }
