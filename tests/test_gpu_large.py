@@ -82,3 +82,28 @@ def test_backward_dx_with_a_2gib_gradient(orc):
     for got, ref, name in ((tensor_f64(dA), dAr * (M // BLOCK), "dA"), (tensor_f64(dB), dBr * (M // BLOCK), "dB")):
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         assert rel <= 5e-3, f"{name}: relative Frobenius error {rel:.3e}"
+
+
+def test_dual_projection_slices_a_2gib_activation(orc):
+    """The dual forward cuts M into slices whose X fits the 32-bit offsets
+    (here two: 261632 rows and 512); rows on both sides of the cut against the
+    oracle, per projection and for silu(G) U."""
+    M, N, K, r, alpha = 262144, 320, 4096, 16, 32.0
+    cfg, wg, Wg, Ag, Bg = _layer(orc, N, K, r, alpha, seed=45)
+    _, wu, Wu, Au, Bu = _layer(orc, N, K, r, alpha, seed=46)
+    Xs = si.activations(cfg, 0)
+    X = bf16_tensor(Xs).repeat(M // BLOCK, 1)
+    t = [bf16_tensor(a) for a in (Ag, Bg, Au, Bu)]
+    log(f"[large dual] M={M} N={N} K={K} r={r}")
+    Yg, Yu, Tg, Tu = q.qlora_dual_fwd(wg, wu, X, *t, alpha)
+    H, _, _ = q.qlora_dual_fwd(wg, wu, X, *t, alpha, swiglu=True)
+    torch.cuda.synchronize()
+    rows = sorted(set(_rows(M, 3)) | {261631, 261632, 261633})
+    xr = Xs[[m % BLOCK for m in rows]]
+    Gr, Tgr = orc.qlora_fwd(Wg, xr, Ag, Bg, alpha)
+    Ur, Tur = orc.qlora_fwd(Wu, xr, Au, Bu, alpha)
+    sel = torch.tensor(rows, device="cuda")
+    assert_close(tensor_f64(Yg.index_select(0, sel)), Gr, "Y_gate rows")
+    assert_close(tensor_f64(Yu.index_select(0, sel)), Ur, "Y_up rows")
+    assert_close(Tg.index_select(0, sel).cpu().numpy(), Tgr, "T_gate rows")
+    assert_close(tensor_f64(H.index_select(0, sel)), orc.swiglu(Gr, Ur), "H rows")
