@@ -97,45 +97,65 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 // ---------------------------------------------------------------------------
 // dequantization of one 64-code block (32 bytes) into 32 bf16 pairs
 // ---------------------------------------------------------------------------
+// The two lanes that share a block (lanes 2i and 2i + 1 of a wave) build its
+// table together: lane parity p scales the 8 levels 8p .. 8p + 7 and takes
+// the other 8 from its partner with a DPP move.  Entries 0..7 of a lane's
+// table are its own levels, so lane 1 of a pair looks codes up with bit 3
+// flipped (the flip argument of dequant8), which lands every code on its own
+// level.
 struct Table {
   uint32_t lo[4], hi[4];   // low / high bytes of the 16 bf16 values, 4 per word
 };
 
-__device__ __forceinline__ Table make_table(const float (&lv)[16], float sc) {
-  uint32_t P[8];
+__device__ __forceinline__ uint32_t dpp_pair_swap(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, DPP_QUAD_XOR1, 0xF, 0xF, false);
+}
+
+// mv: this lane's 8 levels; sc: the block's scale
+__device__ __forceinline__ Table make_table(const float (&mv)[8], float sc) {
+  uint32_t P[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) P[j] = pack_bf16x2(lv[2 * j] * sc, lv[2 * j + 1] * sc);
+  for (int j = 0; j < 4; ++j) P[j] = pack_bf16x2(mv[2 * j] * sc, mv[2 * j + 1] * sc);
   Table t;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     t.lo[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x06040200u);
     t.hi[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x07050301u);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    t.lo[2 + q] = dpp_pair_swap(t.lo[q]);
+    t.hi[2 + q] = dpp_pair_swap(t.hi[q]);
   }
   return t;
 }
 
-// four 4-bit indices (one per byte) -> their bf16 low bytes and high bytes
+// four 4-bit indices (one per byte) -> their bf16 low bytes and high bytes.
+// Byte selectors past 12 read as 0xFF, so each half of the table is looked
+// up with the other half's indices pushed past 16 and the two are AND-ed.
 __device__ __forceinline__ void lookup4(const Table& t, uint32_t idx, uint32_t& lo, uint32_t& hi) {
-  const uint32_t m8 = idx & 0x08080808u;
-  const uint32_t selA = idx + (m8 << 1);          // codes 0..7 -> 0..7, codes 8..15 -> 24..31 (0xFF)
-  const uint32_t selB = selA ^ 0x18181818u;       // codes 8..15 -> 0..7, codes 0..7 -> 24..31 (0xFF)
+  // idx | ((idx << 1) & 0x10101010) as one three-input bit operation
+  const uint32_t selA = __builtin_amdgcn_bitop3_b32(idx, idx << 1, 0x10101010u, 0xF8);  // 8..15 -> 24..31 (0xFF)
+  const uint32_t selB = selA ^ 0x18181818u;                // indices 0..7 -> 24..31, 8..15 -> 0..7
   lo = __builtin_amdgcn_perm(t.lo[1], t.lo[0], selA) & __builtin_amdgcn_perm(t.lo[3], t.lo[2], selB);
   hi = __builtin_amdgcn_perm(t.hi[1], t.hi[0], selA) & __builtin_amdgcn_perm(t.hi[3], t.hi[2], selB);
 }
 
-// 8 codes (one word, element e in bits 4e..4e+3) -> 4 words of bf16 pairs in element order
-__device__ __forceinline__ void dequant8(const Table& t, uint32_t c, uint32_t o[4]) {
-  uint32_t le, he, lo_, ho;
-  lookup4(t, c & 0x0F0F0F0Fu, le, he);            // elements 0, 2, 4, 6
-  lookup4(t, (c >> 4) & 0x0F0F0F0Fu, lo_, ho);    // elements 1, 3, 5, 7
-  const uint32_t e02 = __builtin_amdgcn_perm(he, le, 0x05010400u);
-  const uint32_t e46 = __builtin_amdgcn_perm(he, le, 0x07030602u);
-  const uint32_t o13 = __builtin_amdgcn_perm(ho, lo_, 0x05010400u);
-  const uint32_t o57 = __builtin_amdgcn_perm(ho, lo_, 0x07030602u);
-  o[0] = __builtin_amdgcn_perm(o13, e02, 0x05040100u);
-  o[1] = __builtin_amdgcn_perm(o13, e02, 0x07060302u);
-  o[2] = __builtin_amdgcn_perm(o57, e46, 0x05040100u);
-  o[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);
+// 8 codes (one word, element e in bits 4e..4e+3) -> 4 words of bf16 pairs in
+// element order.  The codes are first regrouped one per byte in element order
+// (bytes of c and c >> 4 interleaved, then masked), so that each lookup's
+// bytes pair up directly into two output words.
+__device__ __forceinline__ void dequant8(const Table& t, uint32_t c, uint32_t flip, uint32_t o[4]) {
+  const uint32_t c4 = c >> 4;
+  const uint32_t i03 = (__builtin_amdgcn_perm(c4, c, 0x05010400u) ^ flip) & 0x0F0F0F0Fu;   // codes 0..3
+  const uint32_t i47 = (__builtin_amdgcn_perm(c4, c, 0x07030602u) ^ flip) & 0x0F0F0F0Fu;   // codes 4..7
+  uint32_t l, h;
+  lookup4(t, i03, l, h);
+  o[0] = __builtin_amdgcn_perm(h, l, 0x05010400u);
+  o[1] = __builtin_amdgcn_perm(h, l, 0x07030602u);
+  lookup4(t, i47, l, h);
+  o[2] = __builtin_amdgcn_perm(h, l, 0x05010400u);
+  o[3] = __builtin_amdgcn_perm(h, l, 0x07030602u);
 }
 
 // ---------------------------------------------------------------------------
@@ -189,7 +209,7 @@ __device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, ui
 // fl32(E4M3(q) * d); with fp32 scales q reads 0 from an empty buffer and the
 // OR makes it E4M3(1.0), so the product is the stored scale exactly
 __device__ __forceinline__ float stage_scale(const StageW& st, uint32_t qor) {
-  return e4m3_decode(st.q | qor) * st.d;
+  return __builtin_amdgcn_cvt_f32_fp8((int)(st.q | qor), 0) * st.d;
 }
 
 __device__ __forceinline__ void store_a(const StageA& st, u16* sA, int tid) {
@@ -263,14 +283,14 @@ __device__ __forceinline__ u16* w_dst(u16* sB, int tid) {
 }
 
 // dequantize the thread's half block and store its 32 bf16 values at dst
-__device__ __forceinline__ void store_w(const StageW& st, const float (&lv)[16], uint32_t qor,
-                                        u16* dst) {
-  const Table t = make_table(lv, stage_scale(st, qor));
+__device__ __forceinline__ void store_w(const StageW& st, const float (&mv)[8], uint32_t flip,
+                                        uint32_t qor, u16* dst) {
+  const Table t = make_table(mv, stage_scale(st, qor));
   const uint32_t c[4] = {st.c.x, st.c.y, st.c.z, st.c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t o[4];
-    dequant8(t, c[i], o);
+    dequant8(t, c[i], flip, o);
     *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
@@ -404,10 +424,11 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
                                                const u16* sB, int wm, int wn, int lane,
                                                StageA& ra, StageW& w,
                                                u16* sA_next, u16* wdst_next, int tid,
-                                               const NextLoads& nl, const float (&lv)[16]) {
+                                               const NextLoads& nl, const float (&mv)[8],
+                                               uint32_t flip) {
   bf16x8_t fa[2][4], fb[2][2];
   frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
-  const Table t = make_table(lv, stage_scale(w, nl.bf->qor));
+  const Table t = make_table(mv, stage_scale(w, nl.bf->qor));
   const uint32_t c[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
   {
     // the scale byte and group constant of the weight block after next
@@ -429,7 +450,7 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
                                                             0, 0, 0);
     {
       uint32_t o[4];
-      dequant8(t, c[ks], o);
+      dequant8(t, c[ks], flip, o);
       *reinterpret_cast<uint4*>(wdst_next + 8 * ks) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(sA_next + (tid / 8 + 64 * ks) * APITCH + (tid % 8) * 8) = ra.v[ks];
       ra.v[ks] = bload16(nl.bf->a, nl.a_base + ks * nl.a_step + 2 * nl.a_c0);
@@ -505,9 +526,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
                                                              : (wv.N * wv.K / 64 + 255) / 256)));
   bf.qor = wv.fp32_scale ? 0x38u : 0u;   // E4M3 code of 1.0
   bf.dshift = wv.fp32_scale ? 0u : 8u;
-  float lv[16];
+  // this lane's half of the block table: levels 8p .. 8p + 7 for lane parity p
+  const bool odd_lane = tid & 1;
+  const uint32_t flip = odd_lane ? 0x08080808u : 0u;
+  float mv[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = wv.lv[i];
+  for (int i = 0; i < 8; ++i) mv[i] = odd_lane ? wv.lv[8 + i] : wv.lv[i];
   const uint32_t K = (uint32_t)p.w.K;
   // rows past M give offsets past the end (the host checks 32-bit room)
   const uint32_t a_base = (uint32_t)((m0 + tid / 8) * p.lda * 2) + 2 * 8 * (tid % 8);
@@ -533,7 +557,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   load_a(ra, bf, a_base, a_step, 0);
   load_w(w0, bf, w_n(0), w_k(0), whalf, K, true);
   store_a(ra, sA[0], tid);
-  store_w(w0, lv, bf.qor, wdst0);
+  store_w(w0, mv, flip, bf.qor, wdst0);
   load_a(ra, bf, a_base, a_step, BK);
   load_w(w1, bf, w_n(1), w_k(1), whalf, K, 1 < nk);
   load_w(w0, bf, w_n(2), w_k(2), whalf, K, 2 < nk);
@@ -546,14 +570,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
     {
       const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 2) * BK), w_n(kt + 3), w_k(kt + 3), whalf, K,
                          kt + 3 < nk};
-      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl, lv);
+      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl, mv, flip);
     }
     __syncthreads();
     // buffer 1 holds stage kt+1; ra = A(kt+2), w0 = W(kt+2), w1 = W(kt+3)
     {
       const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 3) * BK), w_n(kt + 4), w_k(kt + 4), whalf, K,
                          kt + 4 < nk};
-      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl, lv);
+      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl, mv, flip);
     }
     __syncthreads();
   }

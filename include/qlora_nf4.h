@@ -81,7 +81,9 @@ enum { QL_CODEBOOK_NF4 = 0, QL_CODEBOOK_INT4 = 1 };
  *  block  : must be 64 (block b covers flattened elements [64b, 64b+64),
  *           always inside one row because K % 64 == 0); nb = N*K/64.
  *  dq_block = 256 (double quantization, the QLoRA default):
- *    qscale : nb bytes, OCP FP8 E4M3 code of each block's scale;
+ *    qscale : nb bytes, OCP FP8 E4M3 code of each block's scale, at most
+ *             0x7E (448, what nf4_quantize writes; the sign bit and the
+ *             E4M3 NaN code 0x7F are not valid scales);
  *    dscale : ng = ceil(nb/256) fp32; group g covers blocks [256g, 256g+256)
  *             (the last may be shorter); restored block scale is
  *             fl32(E4M3(qscale[b]) * dscale[b/256]).
