@@ -8,11 +8,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 namespace qln {
 
 typedef uint16_t u16;
 
 constexpr int QLN_MAX_RANK = 128;   // largest LoRA rank the kernels take
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per (kernel, device) pair; safe to call from several host threads.  Kernels
+// that take more than the default dynamic LDS call this before each launch.
+inline hipError_t set_dynamic_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
 
 // The 16 NF4 levels as fp32 bit patterns, code order.  Ultralytics glossary
 // "QLoRA", "How QLoRA works" (the level-building snippet): normal quantiles at

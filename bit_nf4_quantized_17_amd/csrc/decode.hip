@@ -650,28 +650,25 @@ static hipError_t launch_one(const DecArgs& p, hipStream_t st) {
   const int nbk = (int)(p.w.K / 64);
   const int npair = (nbk + 1) / 2;
   const Lds L = lds_layout(TILES, wave_pairs_max((npair + p.kparts - 1) / p.kparts), p.r);
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<TILES>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)MAX_DYN_LDS);
-  });
+  const hipError_t attr = set_dynamic_lds(reinterpret_cast<const void*>(&k_decode<TILES>), (int)MAX_DYN_LDS);
   if (attr != hipSuccess) return attr;
   const unsigned grid = (unsigned)(p.gcols * p.kparts);
   hipLaunchKernelGGL((k_decode<TILES>), dim3(grid), dim3(NTHREADS), L.total, st, p);
   return hipGetLastError();
 }
 
+// compute units of the current device (queried once per device; 256, the
+// MI355X count, if the query fails)
 static int device_cus() {
-  static int cus = 0;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  });
-  return cus;
+  constexpr int MAX_DEV = 64;
+  static std::atomic<int> cus[MAX_DEV];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cus[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Shape of the weight stream: TILES 16-column tiles per workgroup and the

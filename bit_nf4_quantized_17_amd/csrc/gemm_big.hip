@@ -457,11 +457,13 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
     }
     if (ks == 3) w.c = bload16(nl.bf->codes, nl.wn * (nl.K / 2) + nl.wk / 2 + 16 * nl.whalf);
 #ifndef QLN_NO_INTERLEAVE
-    // keep the dequantization's VALU work between the MFMAs
+    // keep the dequantization's VALU work between the MFMAs (up to five VALU
+    // per MFMA in the forward, six in the backward, as measured best)
+    constexpr int ILV_VALU = MODE == MODE_FWD ? 5 : 6;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, ILV_VALU, 0);   // then VALU
       if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // next fragments
       else if (i < 7) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);             // LDS stores
       else __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                         // global loads
@@ -650,14 +652,8 @@ static bool vec_ok(const void* ptr, int64_t ld) {
 
 template <int MODE, int DUAL = DUAL_NONE>
 static hipError_t launch(const BigArgs& p, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<MODE, DUAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_bytes<MODE>());
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  const hipError_t e = set_dynamic_lds((const void*)k_gemm_big<MODE, DUAL>, (int)lds_bytes<MODE>());
+  if (e != hipSuccess) return e;
   const int64_t bn = DUAL ? BN / 2 : BN;
   dim3 grid((unsigned)((p.M + BM - 1) / BM), (unsigned)((p.J + bn - 1) / bn), 1);
   hipLaunchKernelGGL((k_gemm_big<MODE, DUAL>), grid, dim3(NTHREADS), lds_bytes<MODE>(), st, p);

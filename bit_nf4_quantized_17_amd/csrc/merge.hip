@@ -251,12 +251,8 @@ __global__ __launch_bounds__(NTHREADS) void k_merge(MergeArgs p) {
 template <bool UNMERGE>
 static hipError_t launch(const MergeArgs& p, hipStream_t st) {
   const size_t lds = lds_bytes(p.r);
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge<UNMERGE>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes(QLN_MAX_RANK));
-  });
+  const hipError_t attr =
+      set_dynamic_lds(reinterpret_cast<const void*>(&k_merge<UNMERGE>), (int)lds_bytes(QLN_MAX_RANK));
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((p.K + TK - 1) / TK), (unsigned)((p.N + TN - 1) / TN));
   hipLaunchKernelGGL((k_merge<UNMERGE>), grid, dim3(NTHREADS), lds, st, p);
