@@ -42,7 +42,11 @@
  *  - Preconditions that are documented, not checked: inputs are finite;
  *    outputs do not overlap inputs or each other.
  *  - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
- *  - Stateless: concurrent calls on different streams are safe.
+ *  - Stateless: the library keeps no per-call state between calls, so
+ *    concurrent calls on different streams are safe as long as they do not
+ *    share a workspace or an output buffer.  A workspace is scratch for one
+ *    call at a time; the decode path hands partial sums between its
+ *    workgroups through it.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
