@@ -183,7 +183,7 @@ def bench_decode(hip, reps=60):
     import bit_nf4_quantized_17_amd as q
     import synthetic_inputs as si
     from tests.helpers import bf16_tensor
-    cfg = si.CONFIGS["c5"]
+    cfg = si.CONFIGS["decode_8192_28672"]
     out = []
     st = torch.cuda.current_stream().cuda_stream
     for li, L in enumerate(cfg.layers):
@@ -510,7 +510,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": a.numel() * 4, "copies": 3}))
         return
     hip = Hip()
-    cfg = si.CONFIGS["c4"]
+    cfg = si.CONFIGS["mlp70b_28672"]
     log("[bench] generating the 70B-class MLP slice inputs")
     layers = [Layer(cfg, 0), Layer(cfg, 1)]
     up, down = layers

@@ -52,17 +52,17 @@ class Config:
 
 
 CONFIGS: Dict[str, Config] = {
-    "c1": Config("c1", "tiny QLoRA linear 256x256, 16 tokens, r=8",
+    "tiny_256": Config("tiny_256", "tiny QLoRA linear 256x256, 16 tokens, r=8",
                  [Layer("proj", 256, 256)], M=16, r=8, alpha=16.0),
-    "c2": Config("c2", "7B-class attention projection 4096x4096, 4096 tokens, r=16",
+    "attn_4096": Config("attn_4096", "7B-class attention projection 4096x4096, 4096 tokens, r=16",
                  [Layer("attn", 4096, 4096)], M=4096, r=16, alpha=32.0),
-    "c3": Config("c3", "7B-class MLP gate/up 4096->11008, down 11008->4096, 8192 tokens, r=64",
+    "mlp7b_11008": Config("mlp7b_11008", "7B-class MLP gate/up 4096->11008, down 11008->4096, 8192 tokens, r=64",
                  [Layer("gate", 11008, 4096), Layer("up", 11008, 4096), Layer("down", 4096, 11008)],
                  M=8192, r=64, alpha=16.0),
-    "c4": Config("c4", "70B-class MLP slice up 8192->28672, down 28672->8192, 4096 tokens, r=64",
+    "mlp70b_28672": Config("mlp70b_28672", "70B-class MLP slice up 8192->28672, down 28672->8192, 4096 tokens, r=64",
                  [Layer("up", 28672, 8192), Layer("down", 8192, 28672)],
                  M=4096, r=64, alpha=16.0, outlier_frac=0.01),
-    "c5": Config("c5", "decode: W 8192x8192 and 28672x8192, M in {1,4,16}, r=16",
+    "decode_8192_28672": Config("decode_8192_28672", "decode: W 8192x8192 and 28672x8192, M in {1,4,16}, r=16",
                  [Layer("sq", 8192, 8192), Layer("up", 28672, 8192)],
                  M=16, r=16, alpha=32.0, decode_M=(1, 4, 16)),
 }

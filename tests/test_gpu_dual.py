@@ -94,7 +94,7 @@ def test_dual_full_size_sampled_rows(orc):
     """Gate and up projections of the 70B-class MLP (two 28672x8192 weights,
     4096 tokens, r = 64): the whole dual forward on the GPU, sampled rows of
     G, U and H against the oracle."""
-    cfg = si.CONFIGS["c4"]
+    cfg = si.CONFIGS["mlp70b_28672"]
     gate = GpuLayer(cfg, 0)
     up_cfg = si.custom(N=gate.N, K=gate.K, M=gate.M, r=gate.r, alpha=gate.alpha, seed=cfg.seed + 101,
                        outlier_frac=cfg.outlier_frac)

@@ -113,7 +113,7 @@ def test_merge_with_zero_adapter_is_dequantize(orc):
 def test_merge_full_size_sampled_rows(orc):
     """The 70B-class up projection (28672x8192, r = 64): the whole merge on the
     GPU, sampled rows against the oracle."""
-    cfg = si.CONFIGS["c4"]
+    cfg = si.CONFIGS["mlp70b_28672"]
     lay = GpuLayer(cfg, 0, M=1)
     N, K, alpha = lay.N, lay.K, lay.alpha
     log(f"[merge full size] {N}x{K} r={lay.r}")

@@ -265,8 +265,8 @@ def _check_layer_full_size(orc, cfg, li, M=None, bwd=True):
     assert_close(np.array([gb[n, j] for n, j in ib]), eb, f"{label} dB entries")
 
 
-@pytest.mark.parametrize("key,li", [("c1", 0), ("c2", 0), ("c3", 0), ("c3", 2), ("c4", 0),
-                                    ("c4", 1)])
+@pytest.mark.parametrize("key,li", [("tiny_256", 0), ("attn_4096", 0), ("mlp7b_11008", 0), ("mlp7b_11008", 2), ("mlp70b_28672", 0),
+                                    ("mlp70b_28672", 1)])
 def test_workload_shapes(orc, key, li):
     _check_layer_full_size(orc, si.CONFIGS[key], li)
 
@@ -274,4 +274,4 @@ def test_workload_shapes(orc, key, li):
 @pytest.mark.parametrize("li", [0, 1])
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_shapes(orc, li, M):
-    _check_layer_full_size(orc, si.CONFIGS["c5"], li, M=M, bwd=False)
+    _check_layer_full_size(orc, si.CONFIGS["decode_8192_28672"], li, M=M, bwd=False)
