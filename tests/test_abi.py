@@ -241,3 +241,17 @@ def test_adamw_rejects_bad_arguments():
     assert call((T * 1)(T(FAKE, FAKE, FAKE + 4, FAKE, None, 8))) == -4
     assert call((T * 1)(T(FAKE, FAKE, FAKE, FAKE, FAKE + 8, 8))) == -4
     assert call((T * 1)(T(None, None, None, None, None, 0))) != -1   # empty tensors need no buffers
+
+
+def test_binding_raises_without_the_library(monkeypatch, tmp_path):
+    """The binding has no fallback: with the shared library absent, loading it
+    and every call through it raise instead of computing anything."""
+    import bit_nf4_quantized_17_amd as q
+    monkeypatch.setattr(q, "_lib", None)
+    monkeypatch.setattr(q, "LIB_PATH", str(tmp_path / "libqlora_nf4.so"))
+    with pytest.raises(ImportError):
+        q.lib()
+    with pytest.raises(ImportError):
+        q.nf4_levels()
+    with pytest.raises(ImportError):
+        q.codebook_levels("int4")
