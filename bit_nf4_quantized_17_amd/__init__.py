@@ -164,7 +164,24 @@ class NF4Weight:
     def double_quant(self) -> bool:
         return self.qscale is not None
 
+    def validate(self) -> None:
+        """Raise ValueError unless every buffer is a contiguous cuda tensor of the
+        dtype and element count nf4_storage_bytes gives for [rows][cols], all on
+        one device: the kernels index these buffers by the descriptor's shape."""
+        import torch
+        if self.codebook not in CODEBOOKS:
+            raise ValueError(f"unknown codebook {self.codebook!r}")
+        c, q, d = nf4_storage_bytes(self.rows, self.cols, 64, 256 if self.double_quant else 0)
+        _need(self.codes, torch.uint8, (c,), "codes")
+        if self.qscale is not None:
+            _need(self.qscale, torch.uint8, (q,), "qscale")
+        _need(self.dscale, torch.float32, (d // 4,), "dscale")
+        devs = {t.device for t in (self.codes, self.qscale, self.dscale) if t is not None}
+        if len(devs) != 1:
+            raise ValueError(f"weight buffers are on different devices: {sorted(map(str, devs))}")
+
     def descriptor(self) -> _Weight:
+        self.validate()
         return _Weight(self.codes.data_ptr(), _ptr(self.qscale), self.dscale.data_ptr(),
                        self.rows, self.cols, 64, 256 if self.double_quant else 0,
                        CODEBOOKS[self.codebook])
@@ -192,6 +209,11 @@ def nf4_quantize(W, out: Optional[NF4Weight] = None, absmax=None, stream=None,
     w = out
     if w.codebook != codebook or w.double_quant != double_quant:
         raise ValueError("out has another codebook or scale format")
+    if (w.rows, w.cols) != (rows, cols):
+        raise ValueError(f"out holds a {w.rows}x{w.cols} weight, W is {rows}x{cols}")
+    w.validate()
+    if absmax is not None:
+        _need(absmax, torch.float32, (rows * cols // 64,), "absmax")
     _check(lib().qlora_quantize(W.data_ptr(), rows, cols, CODEBOOKS[codebook],
                                 256 if double_quant else 0, w.codes.data_ptr(), _ptr(w.qscale),
                                 w.dscale.data_ptr(), _ptr(absmax), _stream(stream)))

@@ -42,11 +42,12 @@
  *  - Preconditions that are documented, not checked: inputs are finite;
  *    outputs do not overlap inputs or each other.
  *  - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
- *  - Stateless: the library keeps no per-call state between calls, so
+ *  - Library state: the compute calls keep no state between calls, so
  *    concurrent calls on different streams are safe as long as they do not
- *    share a workspace or an output buffer.  A workspace is scratch for one
- *    call at a time; the decode path hands partial sums between its
- *    workgroups through it.
+ *    share a workspace or an output buffer (a workspace is scratch for one
+ *    call at a time).  The one piece of state is the benchmark timing hook of
+ *    qlora_set_timing_events: thread-local HIP event handles that later
+ *    calls on the same thread record; it is empty unless a caller sets it.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H

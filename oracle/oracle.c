@@ -409,7 +409,9 @@ int oracle_qlora_bwd_dx(const uint16_t* Wdq, int64_t N, int64_t K,
   return 0;
 }
 
-/* T = X A^T and U = dY B in double, one row of M per task. */
+/* T = X A^T and U = dY B in double, one row of M per task.  Every element  */
+/* is one sum in increasing contraction order (k for T, n for U); U keeps a  */
+/* running sum per rank and walks dY and B row by row.                       */
 typedef struct {
   int64_t N, K; const uint16_t* X; const uint16_t* dY; const uint16_t* A; const uint16_t* B;
   int r; double* T; double* U;
@@ -419,13 +421,17 @@ static void tu_range(void* p, int64_t m0, int64_t m1) {
   tu_ctx* c = (tu_ctx*)p;
   for (int64_t m = m0; m < m1; ++m) {
     for (int j = 0; j < c->r; ++j) {
-      double t = 0.0, u = 0.0;
+      double t = 0.0;
       for (int64_t k = 0; k < c->K; ++k)
         t += bf16_to_double(c->X[m * c->K + k]) * bf16_to_double(c->A[(int64_t)j * c->K + k]);
-      for (int64_t n = 0; n < c->N; ++n)
-        u += bf16_to_double(c->dY[m * c->N + n]) * bf16_to_double(c->B[n * c->r + j]);
       c->T[m * c->r + j] = t;
-      c->U[m * c->r + j] = u;
+    }
+    double* u = c->U + m * c->r;
+    for (int j = 0; j < c->r; ++j) u[j] = 0.0;
+    for (int64_t n = 0; n < c->N; ++n) {
+      const double g = bf16_to_double(c->dY[m * c->N + n]);
+      const uint16_t* b = c->B + n * c->r;
+      for (int j = 0; j < c->r; ++j) u[j] += g * bf16_to_double(b[j]);
     }
   }
 }
@@ -435,30 +441,50 @@ typedef struct {
   const double* T; const double* U; double* dA; double* dB;
 } ad_ctx;
 
-/* tasks [0, K) compute column k of dA; tasks [K, K+N) compute row n of dB */
+/* Columns of dA and rows of dB in chunks of AD_CHUNK: tasks [0, ka) take    */
+/* columns [AD_CHUNK t, AD_CHUNK t + AD_CHUNK) of dA, tasks [ka, ka + nb)    */
+/* rows of dB.  Each element is one sum over m in increasing order;          */
+/* walking m in the outer loop keeps the reads of X, dY, U and T sequential. */
+#define AD_CHUNK 32
 static void ad_range(void* p, int64_t t0, int64_t t1) {
   ad_ctx* c = (ad_ctx*)p;
+  const int64_t ka = (c->K + AD_CHUNK - 1) / AD_CHUNK;
+  double* acc = (double*)malloc((size_t)c->r * AD_CHUNK * sizeof(double));
+  if (!acc) abort();   /* no result is better than a wrong one */
   for (int64_t t = t0; t < t1; ++t) {
-    if (t < c->K) {
-      int64_t k = t;
+    if (t < ka) {
       if (!c->dA) continue;
-      for (int j = 0; j < c->r; ++j) {
-        double acc = 0.0;
-        for (int64_t m = 0; m < c->M; ++m)
-          acc += c->U[m * c->r + j] * bf16_to_double(c->X[m * c->K + k]);
-        c->dA[(int64_t)j * c->K + k] = c->s * acc;
+      const int64_t k0 = t * AD_CHUNK, kn = (c->K - k0 < AD_CHUNK) ? c->K - k0 : AD_CHUNK;
+      for (int64_t i = 0; i < (int64_t)c->r * AD_CHUNK; ++i) acc[i] = 0.0;
+      for (int64_t m = 0; m < c->M; ++m) {
+        const uint16_t* x = c->X + m * c->K + k0;
+        const double* u = c->U + m * c->r;
+        for (int j = 0; j < c->r; ++j) {
+          double* a = acc + (int64_t)j * AD_CHUNK;
+          for (int64_t kk = 0; kk < kn; ++kk) a[kk] += u[j] * bf16_to_double(x[kk]);
+        }
       }
+      for (int j = 0; j < c->r; ++j)
+        for (int64_t kk = 0; kk < kn; ++kk)
+          c->dA[(int64_t)j * c->K + k0 + kk] = c->s * acc[(int64_t)j * AD_CHUNK + kk];
     } else {
-      int64_t n = t - c->K;
       if (!c->dB) continue;
-      for (int j = 0; j < c->r; ++j) {
-        double acc = 0.0;
-        for (int64_t m = 0; m < c->M; ++m)
-          acc += bf16_to_double(c->dY[m * c->N + n]) * c->T[m * c->r + j];
-        c->dB[n * c->r + j] = c->s * acc;
+      const int64_t n0 = (t - ka) * AD_CHUNK, nn = (c->N - n0 < AD_CHUNK) ? c->N - n0 : AD_CHUNK;
+      for (int64_t i = 0; i < (int64_t)c->r * AD_CHUNK; ++i) acc[i] = 0.0;
+      for (int64_t m = 0; m < c->M; ++m) {
+        const uint16_t* g = c->dY + m * c->N + n0;
+        const double* tm = c->T + m * c->r;
+        for (int64_t i = 0; i < nn; ++i) {
+          const double gv = bf16_to_double(g[i]);
+          double* a = acc + i * c->r;
+          for (int j = 0; j < c->r; ++j) a[j] += gv * tm[j];
+        }
       }
+      for (int64_t i = 0; i < nn; ++i)
+        for (int j = 0; j < c->r; ++j) c->dB[(n0 + i) * c->r + j] = c->s * acc[i * c->r + j];
     }
   }
+  free(acc);
 }
 
 int oracle_qlora_bwd_adapters(int64_t N, int64_t K, const uint16_t* X, const uint16_t* dY,
@@ -471,7 +497,7 @@ int oracle_qlora_bwd_adapters(int64_t N, int64_t K, const uint16_t* X, const uin
   tu_ctx tc = { N, K, X, dY, A, B, r, T, U };
   parallel_for(M, nthreads, tu_range, &tc);
   ad_ctx ac = { M, N, K, X, dY, r, alpha / (double)r, T, U, dA_out, dB_out };
-  parallel_for(K + N, nthreads, ad_range, &ac);
+  parallel_for((K + AD_CHUNK - 1) / AD_CHUNK + (N + AD_CHUNK - 1) / AD_CHUNK, nthreads, ad_range, &ac);
   free(T);
   free(U);
   return 0;

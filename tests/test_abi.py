@@ -255,3 +255,28 @@ def test_binding_raises_without_the_library(monkeypatch, tmp_path):
         q.nf4_levels()
     with pytest.raises(ImportError):
         q.codebook_levels("int4")
+
+
+def test_binding_validates_weight_buffers():
+    """The binding checks a weight's buffers against its shape before building
+    a descriptor: the kernels index them by rows and cols, so a short or
+    mistyped buffer must never reach the library."""
+    torch = pytest.importorskip("torch")
+    c, qb, d = q.nf4_storage_bytes(128, 256)
+    good = dict(codes=torch.empty(c, dtype=torch.uint8), qscale=torch.empty(qb, dtype=torch.uint8),
+                dscale=torch.empty(d // 4, dtype=torch.float32))
+    cases = [
+        dict(good, codes=torch.empty(c - 16, dtype=torch.uint8)),
+        dict(good, qscale=torch.empty(qb, dtype=torch.int8)),
+        dict(good, dscale=torch.empty(d // 4 + 1, dtype=torch.float32)),
+        dict(good, codes=torch.empty(2 * c, dtype=torch.uint8)[::2]),
+    ]
+    for kw in cases:
+        w = q.NF4Weight(rows=128, cols=256, **kw)
+        with pytest.raises(ValueError):
+            w.descriptor()
+    # well-formed host tensors still fail: the buffers must be device memory
+    with pytest.raises(ValueError, match="cuda"):
+        q.NF4Weight(rows=128, cols=256, **good).descriptor()
+    with pytest.raises(ValueError, match="codebook"):
+        q.NF4Weight(rows=128, cols=256, codebook="fp4", **good).validate()

@@ -120,3 +120,96 @@ def test_adamw_five_steps_with_master(orc):
     assert np.allclose(c.w.cpu().numpy(), th, rtol=1e-5, atol=1e-9)
     assert np.allclose(c.md.cpu().numpy(), m, rtol=1e-5, atol=1e-10)
     assert np.allclose(c.vd.cpu().numpy(), v, rtol=1e-5, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# optimizer state in managed (unified) memory
+# ---------------------------------------------------------------------------
+HIP_ATTR_MANAGED_MEMORY = 24      # hipDeviceAttributeManagedMemory
+HIP_MEM_ATTACH_GLOBAL = 1         # hipMemAttachGlobal
+HIP_MEMCPY_DEFAULT = 4          # hipMemcpyDefault: the runtime tells the directions apart
+
+
+class _Managed:
+    """fp32 arrays in hipMallocManaged memory (attached globally, no prefetch
+    or advice), filled and read back with hipMemcpy.  The HIP runtime's
+    symbols resolve through the library's handle: the runtime torch and the
+    library already share."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        L = q.lib()
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.hipMallocManaged.argtypes = [ctypes.POINTER(vp), sz, ctypes.c_uint]
+        L.hipFree.argtypes = [vp]
+        L.hipMemcpy.argtypes = [vp, vp, sz, ctypes.c_int]
+        L.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+        L.hipDeviceSynchronize.argtypes = []
+        self.L = L
+        self.ptrs = []
+
+    def supported(self) -> bool:
+        v = self.ct.c_int(0)
+        return self.L.hipDeviceGetAttribute(self.ct.byref(v), HIP_ATTR_MANAGED_MEMORY,
+                                            torch.cuda.current_device()) == 0 and v.value == 1
+
+    def array(self, host: np.ndarray) -> int:
+        host = np.ascontiguousarray(host, np.float32)
+        p = self.ct.c_void_p()
+        assert self.L.hipMallocManaged(self.ct.byref(p), max(16, host.nbytes), HIP_MEM_ATTACH_GLOBAL) == 0
+        self.ptrs.append(p.value)
+        assert self.L.hipMemcpy(p.value, host.ctypes.data, host.nbytes, HIP_MEMCPY_DEFAULT) == 0
+        return p.value
+
+    def read(self, ptr: int, n: int) -> np.ndarray:
+        out = np.empty(n, np.float32)
+        assert self.L.hipMemcpy(out.ctypes.data, ptr, out.nbytes, HIP_MEMCPY_DEFAULT) == 0
+        return out
+
+    def free(self):
+        assert self.L.hipDeviceSynchronize() == 0
+        for p in self.ptrs:
+            self.L.hipFree(p)
+        self.ptrs = []
+
+
+def test_adamw_state_in_managed_memory(orc):
+    """Ultralytics "QLoRA" (paged-optimizer bullet) and vnread "Grokking QLoRA"
+    ("Paged Optimizers"): the optimizer state lives in unified memory that the
+    runtime may page.  The moments and fp32 masters here are hipMallocManaged
+    allocations handed to the C ABI as raw pointers; three steps must match the
+    oracle to the same bar as device memory."""
+    mm = _Managed()
+    if not mm.supported():
+        pytest.skip("the device reports no managed-memory support")
+    import ctypes
+    rng = np.random.default_rng(21)
+    sizes = [9, 2049, 64 * 1000 + 5]
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.01
+    try:
+        cases = []
+        for n in sizes:
+            c = Case(n, True, rng)
+            c.mp = mm.array(c.m)
+            c.vp = mm.array(c.v)
+            c.wp = mm.array(c.theta)
+            cases.append(c)
+        T = q._AdamwTensor
+        for step in (1, 2, 3):
+            arr = (T * len(cases))(*[T(c.p.data_ptr(), c.gd.data_ptr(), c.mp, c.vp, c.wp, c.n) for c in cases])
+            log(f"[adamw managed] step {step}")
+            q._check(q.lib().qlora_adamw_step(ctypes.cast(arr, ctypes.c_void_p), len(cases), lr, b1, b2, eps,
+                                             wd, step, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+            torch.cuda.synchronize()
+            for c in cases:
+                # the device-memory checker reads c.md, c.vd, c.w: point them at the managed state
+                c.md = torch.from_numpy(mm.read(c.mp, c.n))
+                c.vd = torch.from_numpy(mm.read(c.vp, c.n))
+                c.w = torch.from_numpy(mm.read(c.wp, c.n))
+            _check(orc, cases, lr, b1, b2, eps, wd, step)
+            for c in cases:   # the next step starts from the state the GPU wrote
+                c.m, c.v = c.md.numpy().copy(), c.vd.numpy().copy()
+                c.theta0 = c.w.numpy().astype(np.float64)
+    finally:
+        mm.free()

@@ -2,9 +2,10 @@
 
 Bit-exact: NF4 codes, E4M3 scale bytes, group constants, exact block absmax
 and dequantized bf16 weights.  Within the fp bar (tests/helpers.py): Y, T,
-dX, dA, dB.  Small shapes are checked in full; the five workload shapes at
-their real sizes are checked on sampled rows / entries, with quantize and
-dequantize still compared in full."""
+dX, dA, dB.  Small shapes are checked in full.  The five workload shapes at
+their real sizes are checked on sampled rows of Y, T and dX (the oracle
+computes those one row at a time) and in full for quantize, dequantize, dA
+and dB."""
 import numpy as np
 import pytest
 
@@ -253,20 +254,15 @@ def _check_layer_full_size(orc, cfg, li, M=None, bwd=True):
     torch.cuda.synchronize()
     dXr = orc.qlora_bwd_dx(Wdq, lay.dY, lay.A, lay.B, lay.alpha, rows=rows)
     assert_close(tensor_f64(dX[rows]), dXr, f"{label} dX rows")
-    rng = np.random.default_rng(li + 11)
-    ia = [(int(j), int(k)) for j, k in zip(rng.integers(0, lay.r, 24), rng.integers(0, lay.K, 24))]
-    ib = [(int(n), int(j)) for n, j in zip(rng.integers(0, lay.N, 24), rng.integers(0, lay.r, 24))]
-    ia += [(0, 0), (lay.r - 1, lay.K - 1)]
-    ib += [(0, 0), (lay.N - 1, lay.r - 1)]
-    ea, eb = orc.qlora_adapter_entries(lay.X, lay.dY, lay.A, lay.B, lay.alpha, ia, ib)
-    ga = tensor_f64(dA)
-    gb = tensor_f64(dB)
-    assert_close(np.array([ga[j, k] for j, k in ia]), ea, f"{label} dA entries")
-    assert_close(np.array([gb[n, j] for n, j in ib]), eb, f"{label} dB entries")
+    # the adapter gradients in full: each entry is a sum over all M tokens
+    log(f"[bwd adapters] {label} dA {lay.r}x{lay.K}, dB {lay.N}x{lay.r} in full")
+    dAr, dBr = orc.qlora_bwd_adapters(lay.X, lay.dY, lay.A, lay.B, lay.alpha)
+    assert_close(tensor_f64(dA), dAr, f"{label} dA")
+    assert_close(tensor_f64(dB), dBr, f"{label} dB")
 
 
-@pytest.mark.parametrize("key,li", [("tiny_256", 0), ("attn_4096", 0), ("mlp7b_11008", 0), ("mlp7b_11008", 2), ("mlp70b_28672", 0),
-                                    ("mlp70b_28672", 1)])
+@pytest.mark.parametrize("key,li", [("tiny_256", 0), ("attn_4096", 0), ("mlp7b_11008", 0), ("mlp7b_11008", 1),
+                                    ("mlp7b_11008", 2), ("mlp70b_28672", 0), ("mlp70b_28672", 1)])
 def test_workload_shapes(orc, key, li):
     _check_layer_full_size(orc, si.CONFIGS[key], li)
 
