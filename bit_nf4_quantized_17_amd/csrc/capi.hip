@@ -96,10 +96,11 @@ int check_layer(const qlora_nf4_weight* w, int64_t M, int r, int compute_dtype) 
   return QL_OK;
 }
 
+// forward workspace: the split-K partials of T (the decode-size kernel needs
+// none, but shapes it does not take run the tiled path)
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  int64_t elems = skinny_partial_elems(M, K, r);
-  if (M <= 16) elems = std::max(elems, decode_workspace_elems(M, N, K, r));
-  return align256((size_t)elems * sizeof(float));
+  (void)N;
+  return align256((size_t)skinny_partial_elems(M, K, r) * sizeof(float));
 }
 
 // backward workspace: U fp32 [M][r] | T fp32 [M][r] (when recomputed) | fp32 split partials
@@ -247,9 +248,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   if (workspace && !aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
-  if (decode_fits(M, view(w), r)) {   // decode sizes: T partials, then the weight stream
+  if (decode_fits(M, view(w), r)) {   // decode sizes: one weight-streaming launch
     record(g_hook.fwd_begin, st);
-    hipError_t e = launch_decode(view(w), X, M, A, B, r, s, Y, T_save, (float*)workspace, st);
+    hipError_t e = launch_decode(view(w), X, M, A, B, r, s, Y, T_save, st);
     record(g_hook.fwd_end, st);
     return hip_status(e, "qlora_linear_fwd: decode launch");
   }

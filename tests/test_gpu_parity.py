@@ -144,25 +144,32 @@ def test_fwd_bwd_small(orc, N, K, M, r, alpha):
     assert_close(tensor_f64(dB), dBr, "dB")
 
 
-# decode-size forwards (M <= 16): the HBM-streaming kernel with every tile
-# count, in-kernel and precomputed T, ragged column tiles and uneven splits of
-# the contraction over the waves
+# decode-size forwards (M <= 16): the weight-streaming kernel over its plans
+# -- 16-row tiles per workgroup TR (1..16), tile groups TG (1..8) and
+# contraction ranges (8 / TG), one or two 16-rank tiles of T, ragged rows in
+# the last workgroup, ranges that hold no 256-wide step, more workgroups than
+# compute units -- and the shapes it leaves to the tiled kernels (r > 32,
+# K % 256 != 0)
 DECODE = [
     # N, K, M, r, alpha
-    (1000, 512, 3, 8, 16.0),        # one block per wave, ragged last tile
-    (4100, 2304, 7, 64, 16.0),      # T precomputed; 36 blocks over 8 waves
-    (50, 768, 16, 128, 8.0),        # maximum rank, fewer rows than one tile
-    (2048, 11008, 16, 32, 32.0),    # two rank tiles of T in-kernel; K % 256 != 0
-    (28672, 1024, 1, 16, 32.0),     # seven column tiles per workgroup
-    (40000, 256, 4, 24, 16.0),      # eight tiles per workgroup, more than one round
-    (12000, 4096, 16, 16, 32.0),    # three tiles per workgroup
-    (4100, 4096, 9, 24, 16.0),      # three tiles, two parts, ragged last column group
-    (2000, 2048, 1, 8, 16.0),       # one tile, a single token
-    (6000, 8192, 16, 64, 16.0),     # three tiles, two parts, four rank tiles of T
-    (1024, 16384, 1, 16, 32.0),     # one tile, four parts, a single token
-    (3000, 16384, 9, 24, 16.0),     # three tiles, four parts, ragged last column group
-    (1001, 768, 5, 3, 16.0),        # odd N*r: the last elements of B come apart from its 16-byte chunks
-    (1001, 704, 5, 3, 16.0),        # K % 256 != 0: the prefill kernels serve it
+    (1000, 512, 3, 8, 16.0),        # TR 1: two steps over eight ranges, ragged last workgroup
+    (4100, 2304, 7, 64, 16.0),      # r > 32: tiled kernels
+    (50, 768, 16, 128, 8.0),        # r > 32, fewer rows than one tile: tiled kernels
+    (2048, 11008, 16, 32, 32.0),    # two rank tiles, a group with no weight tile, 43 steps over 4 ranges
+    (28672, 1024, 1, 16, 32.0),     # TR 7, TG 4: the 70B-class row count
+    (40000, 256, 4, 24, 16.0),      # TR 10, TG 8, one step per wave
+    (12000, 4096, 16, 16, 32.0),    # TR 3, TG 2
+    (4100, 4096, 9, 24, 16.0),      # TR 2, two rank tiles, ragged last tile
+    (2000, 2048, 1, 8, 16.0),       # TR 1, a single token
+    (6000, 8192, 16, 64, 16.0),     # r > 32: tiled kernels
+    (1024, 16384, 1, 16, 32.0),     # long contraction, a single token
+    (3000, 16384, 9, 24, 16.0),     # long contraction, two rank tiles
+    (1001, 768, 5, 3, 16.0),        # odd N * r
+    (1001, 704, 5, 3, 16.0),        # K % 256 != 0: tiled kernels
+    (70000, 256, 2, 16, 16.0),      # TR capped at 16: more workgroups than compute units
+    (4269, 4096, 4, 12, 16.0),      # TR 2, ragged rows
+    (20000, 512, 16, 17, 16.0),     # TR 5, TG 4, rank 17: the second rank tile holds one column
+    (8192, 8192, 16, 32, 16.0),     # the 8192 x 8192 layer at rank 32
 ]
 
 
