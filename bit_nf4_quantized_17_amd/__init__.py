@@ -8,7 +8,8 @@ the library is missing or fails to load, every call raises.
 Functions keep the C ABI's names:
   nf4_levels, nf4_storage_bytes, nf4_quantize, nf4_dequantize,
   qlora_fwd_workspace_bytes, qlora_linear_fwd,
-  qlora_bwd_workspace_bytes, qlora_linear_bwd, qlora_abi_version
+  qlora_bwd_workspace_bytes, qlora_linear_bwd, qlora_linear_bwd_noalloc,
+  qlora_abi_version
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ CODEBOOKS = {"nf4": QL_CODEBOOK_NF4, "int4": QL_CODEBOOK_INT4}
 QL_DUAL_SEPARATE = 1
 QL_DUAL_SWIGLU = 2
 QLORA_MAX_RANK = 128
+QLORA_BWD_NOALLOC_MAX_BYTES = 32 << 20
 _STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_UNSUPPORTED",
            -4: "QL_ERR_ALIGN", -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_HIP"}
 
@@ -85,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_workspace_bytes.restype = SZ
     L.qlora_linear_bwd.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P, SZ, P]
     L.qlora_linear_bwd.restype = I
+    L.qlora_linear_bwd_noalloc.argtypes = [WP, P, P, I64, P, P, I, F, I, P, P, P, P, P]
+    L.qlora_linear_bwd_noalloc.restype = I
     L.qlora_merge.argtypes = [WP, P, P, I, F, P, P]
     L.qlora_merge.restype = I
     L.qlora_unmerge.argtypes = [P, I64, I64, P, P, I, F, P, P]
@@ -390,4 +394,31 @@ def qlora_linear_bwd(w: NF4Weight, X, dY, A, B, alpha: float, T=None, want_dX: b
                                   B.data_ptr(), r, float(alpha), QL_DTYPE_BF16, _ptr(T), _ptr(dX),
                                   dA.data_ptr(), dB.data_ptr(), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))
+    return dX, dA, dB
+
+
+def qlora_linear_bwd_noalloc(w: NF4Weight, X, dY, A, B, alpha: float, dX, dA, dB, T=None,
+                             stream=None):
+    """The backward over the library's fixed per-GPU scratch (no workspace,
+    nothing allocated here either: dX (or None), dA [r, K] and dB [N, r] are
+    the caller's bf16 outputs).  Calls that can overlap on one GPU race."""
+    import torch
+    M, K = X.shape
+    r = A.shape[0]
+    N = w.rows
+    _need(X, torch.bfloat16, (M, w.cols), "X")
+    _need(dY, torch.bfloat16, (M, N), "dY")
+    _need(A, torch.bfloat16, (r, K), "A")
+    _need(B, torch.bfloat16, (N, r), "B")
+    if T is not None:
+        _need(T, torch.float32, (M, r), "T")
+    if dX is not None:
+        _need(dX, torch.bfloat16, (M, K), "dX")
+    _need(dA, torch.bfloat16, (r, K), "dA")
+    _need(dB, torch.bfloat16, (N, r), "dB")
+    d = w.descriptor()
+    _check(lib().qlora_linear_bwd_noalloc(ctypes.byref(d), X.data_ptr(), dY.data_ptr(), M,
+                                          A.data_ptr(), B.data_ptr(), r, float(alpha),
+                                          QL_DTYPE_BF16, _ptr(T), _ptr(dX), dA.data_ptr(),
+                                          dB.data_ptr(), _stream(stream)))
     return dX, dA, dB

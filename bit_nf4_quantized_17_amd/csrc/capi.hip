@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 #include <string>
 
@@ -118,6 +119,81 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r) {
   L.part_off = 2 * mr;
   L.total = L.part_off + align256((size_t)parts * sizeof(float));
   return L;
+}
+
+// checks shared by both backward entry points (all but the workspace)
+int check_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+              const uint16_t* A, const uint16_t* B, int r, int compute_dtype, const float* T_saved,
+              const uint16_t* dX, const uint16_t* dA, const uint16_t* dB) {
+  int rc = check_layer(w, M, r, compute_dtype);
+  if (rc) return rc;
+  if (!X || !dY || !A || !B || !dA || !dB) return fail(QL_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+      !aligned16(dB) || (T_saved && !aligned16(T_saved)) || (dX && !aligned16(dX)))
+    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return QL_OK;
+}
+
+// the backward's launches over a workspace of bwd_layout(M, N, K, r).total bytes
+int run_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+            const uint16_t* A, const uint16_t* B, int r, float alpha, const float* T_saved,
+            uint16_t* dX, uint16_t* dA, uint16_t* dB, char* ws, hipStream_t st) {
+  const int64_t N = w->rows, K = w->cols;
+  const BwdLayout L = bwd_layout(M, N, K, r);
+  float* U = (float*)(ws + L.u_off);
+  float* part = (float*)(ws + L.part_off);
+  const float s = alpha / (float)r;
+  const float* T = T_saved;
+  hipError_t e;
+  if (!T) {
+    float* Tw = (float*)(ws + L.t_off);
+    e = launch_lora_down(X, A, M, K, r, part, Tw, st);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: T recompute launch");
+    T = Tw;
+  }
+  e = launch_lora_u(dY, B, M, N, r, part, U, st);
+  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: U launch");
+  e = launch_lora_db(dY, T, M, N, r, s, part, dB, st);
+  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dB launch");
+  if (dX) {
+    record(g_hook.dx_begin, st);
+    e = launch_dx_main(view(w), dY, M, U, A, r, s, dX, st);
+    record(g_hook.dx_end, st);
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dX launch");
+  }
+  e = launch_lora_da(U, X, M, K, r, s, part, dA, st);
+  return hip_status(e, "qlora_linear_bwd: dA launch");
+}
+
+// Scratch of the allocation-free backward: a fixed array in the library's
+// device data, one copy per GPU (made when the code object is loaded on it
+// and held until the process ends).  Its host-side name is a stand-in, not a
+// device address; the address comes from hipGetSymbolAddress, resolved on
+// the first call on each device with that device current and kept per
+// device.  No part of it needs to start at zero: within one call every
+// kernel writes each scratch element before any kernel of the call reads it.
+static __device__ __align__(256) unsigned char scratch[QLORA_BWD_NOALLOC_MAX_BYTES];
+
+int scratch_of_current_device(char** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QL_ERR_UNSUPPORTED, "device %d (the scratch table covers devices 0..%d)", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(QL_ERR_HIP, "qlora_linear_bwd_noalloc: hipGetSymbolAddress(scratch) gave NULL");
+    addr[dev] = (char*)p;
+  }
+  *out = addr[dev];
+  return QL_OK;
 }
 
 }  // namespace
@@ -337,43 +413,32 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
                      const uint16_t* A, const uint16_t* B, int r, float alpha, int compute_dtype,
                      const float* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_layer(w, M, r, compute_dtype);
+  int rc = check_bwd(w, X, dY, M, A, B, r, compute_dtype, T_saved, dX, dA, dB);
   if (rc) return rc;
-  if (!X || !dY || !A || !B || !dA || !dB || !workspace)
-    return fail(QL_ERR_NULL, "a required pointer is NULL");
-  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
-      !aligned16(dB) || !aligned16(workspace) || (T_saved && !aligned16(T_saved)) ||
-      (dX && !aligned16(dX)))
-    return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  const int64_t N = w->rows, K = w->cols;
-  const BwdLayout L = bwd_layout(M, N, K, r);
-  if (workspace_bytes < L.total)
-    return fail(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  float* U = (float*)(ws + L.u_off);
-  float* part = (float*)(ws + L.part_off);
-  const float s = alpha / (float)r;
-  const float* T = T_saved;
-  hipError_t e;
-  if (!T) {
-    float* Tw = (float*)(ws + L.t_off);
-    e = launch_lora_down(X, A, M, K, r, part, Tw, st);
-    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: T recompute launch");
-    T = Tw;
-  }
-  e = launch_lora_u(dY, B, M, N, r, part, U, st);
-  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: U launch");
-  e = launch_lora_db(dY, T, M, N, r, s, part, dB, st);
-  if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dB launch");
-  if (dX) {
-    record(g_hook.dx_begin, st);
-    e = launch_dx_main(view(w), dY, M, U, A, r, s, dX, st);
-    record(g_hook.dx_end, st);
-    if (e != hipSuccess) return hip_status(e, "qlora_linear_bwd: dX launch");
-  }
-  e = launch_lora_da(U, X, M, K, r, s, part, dA, st);
-  return hip_status(e, "qlora_linear_bwd: dA launch");
+  if (!workspace) return fail(QL_ERR_NULL, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t need = bwd_layout(M, w->rows, w->cols, r).total;
+  if (workspace_bytes < need)
+    return fail(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  return run_bwd(w, X, dY, M, A, B, r, alpha, T_saved, dX, dA, dB, (char*)workspace,
+                 (hipStream_t)stream);
+}
+
+int qlora_linear_bwd_noalloc(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             int compute_dtype, const float* T_saved, uint16_t* dX, uint16_t* dA,
+                             uint16_t* dB, void* stream) {
+  int rc = check_bwd(w, X, dY, M, A, B, r, compute_dtype, T_saved, dX, dA, dB);
+  if (rc) return rc;
+  const size_t need = bwd_layout(M, w->rows, w->cols, r).total;
+  if (need > (size_t)QLORA_BWD_NOALLOC_MAX_BYTES)
+    return fail(QL_ERR_WORKSPACE, "the backward needs %zu bytes of scratch; the allocation-free "
+                "entry point holds %zu (use qlora_linear_bwd with a workspace)",
+                need, (size_t)QLORA_BWD_NOALLOC_MAX_BYTES);
+  char* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  return run_bwd(w, X, dY, M, A, B, r, alpha, T_saved, dX, dA, dB, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -45,9 +45,11 @@
  *  - Library state: the compute calls keep no state between calls, so
  *    concurrent calls on different streams are safe as long as they do not
  *    share a workspace or an output buffer (a workspace is scratch for one
- *    call at a time).  The one piece of state is the benchmark timing hook of
- *    qlora_set_timing_events: thread-local HIP event handles that later
- *    calls on the same thread record; it is empty unless a caller sets it.
+ *    call at a time).  Two pieces of state exist: the benchmark timing hook
+ *    of qlora_set_timing_events (thread-local HIP event handles that later
+ *    calls on the same thread record; empty unless a caller sets it), and
+ *    the per-GPU scratch array of qlora_linear_bwd_noalloc, which all calls
+ *    of that entry point on one GPU share.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
@@ -271,6 +273,27 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
                      int compute_dtype, const float* T_saved,
                      uint16_t* dX, uint16_t* dA, uint16_t* dB,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight training loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and checks as qlora_linear_bwd, whose
+ * kernels it runs, minus the workspace: the scratch (U, the recomputed T,
+ * the split partials) lives in a fixed array of QLORA_BWD_NOALLOC_MAX_BYTES
+ * in the library's device data, one copy per GPU, held until the process
+ * ends.  A call whose qlora_bwd_workspace_bytes(M, N, K, r) exceeds that
+ * returns QL_ERR_WORKSPACE and enqueues nothing (32 MiB covers, e.g., M = 8192
+ * tokens of a 28672 x 8192 layer at r = 64).  The call allocates nothing; the
+ * first call on each device (with that device current) looks up the array's
+ * address there, so a caller that captures graphs makes one call before
+ * capturing.  `stream` must belong to the current device.  Every call on a
+ * GPU shares that GPU's array: calls that can overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  The
+ * array's contents are not meaningful between calls. */
+#define QLORA_BWD_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int qlora_linear_bwd_noalloc(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             int compute_dtype, const float* T_saved,
+                             uint16_t* dX, uint16_t* dA, uint16_t* dB, void* stream);
 
 /* Merge the adapter into the weight (IBM "What is LoRA?": after training the
  * low-rank update B A is merged into the pretrained weight, which then runs

@@ -139,6 +139,32 @@ def test_bwd_validation():
     assert _bwd(w, ws=FAKE, wsb=need - 256) == -5
 
 
+def _bwd_noalloc(w, X=FAKE, dY=FAKE, M=16, A=FAKE, B=FAKE, r=8, dtype=1, T=FAKE, dX=FAKE, dA=FAKE,
+                 dB=FAKE):
+    return q.lib().qlora_linear_bwd_noalloc(ctypes.byref(w) if w is not None else None, X, dY, M, A, B,
+                                            r, 16.0, dtype, T, dX, dA, dB, None)
+
+
+def test_bwd_noalloc_validation():
+    w = _weight()
+    assert _bwd_noalloc(None) == -1
+    assert _bwd_noalloc(w, dA=None) == -1
+    assert _bwd_noalloc(w, dY=None) == -1
+    assert _bwd_noalloc(w, M=0) == -2
+    assert _bwd_noalloc(w, r=0) == -3
+    assert _bwd_noalloc(w, dtype=0) == -3
+    assert _bwd_noalloc(w, dX=FAKE + 6) == -4
+    # a shape whose scratch exceeds the fixed array: rejected before any HIP call
+    big = _weight(rows=28672, cols=8192)
+    M, r = 65536, 128
+    assert q.qlora_bwd_workspace_bytes(M, 28672, 8192, r) > q.QLORA_BWD_NOALLOC_MAX_BYTES
+    assert _bwd_noalloc(big, M=M, r=r) == -5
+    assert b"scratch" in q.lib().qlora_last_error()
+    header = open(HEADER).read()
+    assert re.search(r"#define QLORA_BWD_NOALLOC_MAX_BYTES \(\(size_t\)32 << 20\)", header)
+    assert q.QLORA_BWD_NOALLOC_MAX_BYTES == 32 << 20
+
+
 def test_error_message_is_cleared_by_success():
     L = q.lib()
     assert L.nf4_storage_bytes(10, 100, 64, 256, None, None, None) == -2
