@@ -97,11 +97,13 @@ int check_layer(const qlora_nf4_weight* w, int64_t M, int r, int compute_dtype) 
   return QL_OK;
 }
 
-// forward workspace: the split-K partials of T (the decode-size kernel needs
-// none, but shapes it does not take run the tiled path)
+// forward workspace: the split-K partials of T (of the tiled path, or of the
+// decode path at M <= 16)
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   (void)N;
-  return align256((size_t)skinny_partial_elems(M, K, r) * sizeof(float));
+  size_t b = (size_t)skinny_partial_elems(M, K, r) * sizeof(float);
+  if (M <= 16) b = std::max(b, decode_ws_bytes(K, r));
+  return align256(b);
 }
 
 // backward workspace: U fp32 [M][r] | T fp32 [M][r] (when recomputed) | fp32 split partials
@@ -324,9 +326,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   if (workspace && !aligned16(workspace)) return fail(QL_ERR_ALIGN, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
-  if (decode_fits(M, view(w), r)) {   // decode sizes: one weight-streaming launch
+  if (decode_fits(M, view(w), r)) {   // decode sizes: T partials, then one weight-streaming launch
     record(g_hook.fwd_begin, st);
-    hipError_t e = launch_decode(view(w), X, M, A, B, r, s, Y, T_save, st);
+    hipError_t e = launch_decode(view(w), X, M, A, B, r, s, Y, T_save, (float*)workspace, st);
     record(g_hook.fwd_end, st);
     return hip_status(e, "qlora_linear_fwd: decode launch");
   }

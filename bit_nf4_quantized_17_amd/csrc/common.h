@@ -146,9 +146,12 @@ hipError_t launch_fwd_generic(const NF4View& w, const u16* X, int64_t M, const f
 hipError_t launch_dx_generic(const NF4View& w, const u16* dY, int64_t M, const float* U,
                              const u16* A, int r, float s, u16* dX, hipStream_t st);
 
-// Forward at M <= 16 (writes Y and T_save) in one weight-streaming launch
-// with no workspace; decode_fits says whether a shape can take it.
+// Forward at M <= 16 (writes Y and T_save): a small launch for the partial
+// sums of T = X A^T (into the workspace), then one weight-streaming launch;
+// decode_fits says whether a shape can take it, decode_ws_bytes how much
+// workspace it needs.
 bool decode_fits(int64_t M, const NF4View& w, int r);
+size_t decode_ws_bytes(int64_t K, int r);
 // Adapter merge / unmerge (merge.hip): out = bf16(base +/- s B A), base the
 // dequantized NF4 weight or a bf16 weight; merge_fits says whether the 32-bit
 // offsets hold for a shape.
@@ -159,7 +162,7 @@ hipError_t launch_unmerge(const u16* w_in, int64_t N, int64_t K, const u16* A, c
                           float s, u16* out, hipStream_t st);
 
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
-                         int r, float s, u16* Y, float* T_save, hipStream_t st);
+                         int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st);
 
 // Workspace (fp32 elements) the skinny partial sums of one call need.
 int64_t skinny_partial_elems(int64_t I, int64_t C, int r);
