@@ -183,11 +183,18 @@ def codebook_levels(codebook: str) -> np.ndarray:
     return {"nf4": nf4_levels, "int4": int4_levels}[codebook]()
 
 
+DQ_FORMATS = {"e4m3": 1, "uint8": 2}
+
+
+def _dq_mode(double_quant: bool, dq_format: str) -> int:
+    return DQ_FORMATS[dq_format] if double_quant else 0
+
+
 def quantize(W: np.ndarray, codebook: str = "nf4", double_quant: bool = True,
-             threads: int | None = None):
+             threads: int | None = None, dq_format: str = "e4m3"):
     """(codes, qscale or None, dscale, absmax) with a codebook ("nf4" or "int4") and
-    the scale format: double-quantized E4M3 scales with group constants, or (double_quant
-    False) the fp32 block absmax itself in dscale [N*K/64]."""
+    the scale format: double-quantized 8-bit scales ("e4m3" or "uint8") with group
+    constants, or (double_quant False) the fp32 block absmax itself in dscale [N*K/64]."""
     W = np.ascontiguousarray(W, np.float32)
     rows, cols = W.shape
     nb = rows * cols // 64
@@ -196,22 +203,23 @@ def quantize(W: np.ndarray, codebook: str = "nf4", double_quant: bool = True,
     qscale = np.zeros(nb, np.uint8) if double_quant else None
     dscale = np.zeros((nb + 255) // 256 if double_quant else nb, np.float32)
     absmax = np.zeros(nb, np.float32)
-    _check(lib().oracle_quantize(_ptr(W), rows, cols, _ptr(lv), int(double_quant), _ptr(codes),
+    _check(lib().oracle_quantize(_ptr(W), rows, cols, _ptr(lv), _dq_mode(double_quant, dq_format), _ptr(codes),
                                  _ptr(qscale), _ptr(dscale), _ptr(absmax), threads or default_threads()),
            "quantize")
     return codes, qscale, dscale, absmax
 
 
 def dequantize(codes, qscale, dscale, rows: int, cols: int, codebook: str = "nf4",
-               threads: int | None = None):
-    """bf16 bit patterns (uint16 [N, K]); qscale None means fp32 block scales in dscale."""
+               threads: int | None = None, dq_format: str = "e4m3"):
+    """bf16 bit patterns (uint16 [N, K]); qscale None means fp32 block scales in dscale,
+    else 8-bit scales of dq_format ("e4m3" or "uint8") with group constants."""
     codes = np.ascontiguousarray(codes, np.uint8)
     dq = qscale is not None
     qs = np.ascontiguousarray(qscale, np.uint8) if dq else None
     ds = np.ascontiguousarray(dscale, np.float32)
     lv = codebook_levels(codebook)
     out = np.zeros((rows, cols), np.uint16)
-    _check(lib().oracle_dequantize(_ptr(codes), _ptr(qs), _ptr(ds), rows, cols, _ptr(lv), int(dq),
+    _check(lib().oracle_dequantize(_ptr(codes), _ptr(qs), _ptr(ds), rows, cols, _ptr(lv), _dq_mode(dq, dq_format),
                                    _ptr(out), threads or default_threads()), "dequantize")
     return out
 

@@ -202,13 +202,15 @@ int oracle_encode_blocks(const float* W, int64_t rows, int64_t cols,
 /* "Double Quantization": the 8-bit format is FP8.  Reading taken: OCP E4M3, */
 /* each group's largest scale maps to the format's max 448, so the group     */
 /* constant is d = max / 448 and each scale is stored as E4M3(absmax / d).   */
-/* The NF4 codes use the exact fp32 absmax.                                  */
+/* The NF4 codes use the exact fp32 absmax.  The Ultralytics bullet alone     */
+/* ("8 bits") also reads as a plain 8-bit integer grid; that reading is the  */
+/* second-level format 2 (uint8-linear, below).                              */
 /* ------------------------------------------------------------------------ */
 int oracle_quantize(const float* W, int64_t rows, int64_t cols, const float levels[16],
                     int double_quant, uint8_t* codes, uint8_t* qscale, float* dscale,
                     float* absmax_out, int nthreads) {
   if (!W || !levels || !codes || !dscale || (double_quant && !qscale) || rows <= 0 || cols <= 0 ||
-      cols % 64)
+      cols % 64 || double_quant < 0 || double_quant > 2)
     return -1;
   int64_t nb = rows * cols / 64;
   float* a = (float*)malloc((size_t)nb * sizeof(float));
@@ -226,6 +228,19 @@ int oracle_quantize(const float* W, int64_t rows, int64_t cols, const float leve
     int64_t b0 = g * 256, b1 = b0 + 256 < nb ? b0 + 256 : nb;
     float c = 0.0f;
     for (int64_t b = b0; b < b1; ++b) if (a[b] > c) c = a[b];
+    if (double_quant == 2) {
+      /* uint8-linear reading: 256 evenly spaced values 0, d, ..., 255 d with
+       * d = max / 255; each scale goes to the nearest multiple of d (the
+       * fp32 quotient rounded half to even, at most 255) */
+      float d = c / 255.0f;                       /* fp32 division */
+      dscale[g] = d;
+      for (int64_t b = b0; b < b1; ++b) {
+        if (d == 0.0f) { qscale[b] = 0; continue; }
+        float t = rintf(a[b] / d);                /* fp32 division, round half to even */
+        qscale[b] = (uint8_t)(t > 255.0f ? 255.0f : t);
+      }
+      continue;
+    }
     float d = c / 448.0f;                         /* fp32 division */
     dscale[g] = d;
     for (int64_t b = b0; b < b1; ++b)
@@ -268,10 +283,12 @@ typedef struct {
 static void deq_range(void* p, int64_t b0, int64_t b1) {
   deq_ctx* c = (deq_ctx*)p;
   for (int64_t b = b0; b < b1; ++b) {
-    /* E4M3 value (4 significant bits) times an fp32: exact in double, then
-     * rounded once; without double quantization the fp32 scale itself */
-    float s = c->double_quant ? (float)(oracle_e4m3_value(c->qscale[b]) * (double)c->dscale[b / 256])
-                              : c->dscale[b];
+    /* E4M3 value (4 significant bits) or an 8-bit integer times an fp32:
+     * exact in double, then rounded once; without double quantization the
+     * fp32 scale itself */
+    float s = c->double_quant == 1 ? (float)(oracle_e4m3_value(c->qscale[b]) * (double)c->dscale[b / 256])
+            : c->double_quant == 2 ? (float)((double)c->qscale[b] * (double)c->dscale[b / 256])
+                                   : c->dscale[b];
     for (int e = 0; e < 64; ++e) {
       uint8_t byte = c->codes[b * 32 + e / 2];
       int code = (e & 1) ? (byte >> 4) : (byte & 15);
@@ -285,7 +302,7 @@ int oracle_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* 
                       int64_t rows, int64_t cols, const float levels[16], int double_quant,
                       uint16_t* out_bf16, int nthreads) {
   if (!codes || (double_quant && !qscale) || !dscale || !levels || !out_bf16 || rows <= 0 ||
-      cols <= 0 || cols % 64)
+      cols <= 0 || cols % 64 || double_quant < 0 || double_quant > 2)
     return -1;
   deq_ctx c;
   c.codes = codes; c.qscale = qscale; c.dscale = dscale; c.cols = cols; c.out = out_bf16;

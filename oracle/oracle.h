@@ -80,16 +80,20 @@ void oracle_int4_levels(float out[16]);
 
 /* Quantization with a caller-given codebook and scale format.  Transformers
  * "Bitsandbytes" (4-bit section): double quantization of the scales is an
- * option.  double_quant = 1: as oracle_nf4_quantize with these levels.
- * double_quant = 0: dscale [N*K/64] receives each block's exact fp32 absmax
- * and qscale is unused (may be NULL).  An all-zero block gets the code of
- * v = 0 (nearest level, lower code on a tie). */
+ * option.  double_quant = 1: as oracle_nf4_quantize with these levels (E4M3
+ * second level).  double_quant = 2: the uint8-linear reading of the
+ * Ultralytics "QLoRA" double-quantization bullet ("8 bits, blocks of 256"):
+ * per group d_g = fl32(max_b a_b / 255) and q_b = min(255, rint(fl32(a_b /
+ * d_g))) (0 when d_g = 0).  double_quant = 0: dscale [N*K/64] receives each
+ * block's exact fp32 absmax and qscale is unused (may be NULL).  An all-zero
+ * block gets the code of v = 0 (nearest level, lower code on a tie). */
 int oracle_quantize(const float* W, int64_t rows, int64_t cols, const float levels[16],
                     int double_quant, uint8_t* codes, uint8_t* qscale, float* dscale,
                     float* absmax_out, int nthreads);
 
 /* Dequantize with a caller-given codebook: w' = bf16(fl32(L[code] * s_b)),
- * s_b = fl32(E4M3(q_b) * d_g) (double_quant = 1) or the fp32 dscale[b] (0). */
+ * s_b = fl32(E4M3(q_b) * d_g) (double_quant = 1), fl32(q_b * d_g) (2), or
+ * the fp32 dscale[b] (0). */
 int oracle_dequantize(const uint8_t* codes, const uint8_t* qscale, const float* dscale,
                       int64_t rows, int64_t cols, const float levels[16], int double_quant,
                       uint16_t* out_bf16, int nthreads);

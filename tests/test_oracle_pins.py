@@ -242,6 +242,81 @@ def test_double_quant_structure(orc):
         assert rel.max() <= 2.0 ** -4 + 1e-7
 
 
+def _uint8_restored(qs, ds):
+    """q_b * d_g in float64 (exact: 8-bit integer times an fp32)."""
+    return qs.astype(np.float64) * np.repeat(ds.astype(np.float64), 256)[:qs.size]
+
+
+def test_uint8_double_quant_is_a_uniform_8bit_grid(orc):
+    """The uint8-linear reading of "8 bits in blocks of 256" (Ultralytics "QLoRA",
+    double-quantization bullet): per group the 256 values 0, d, ..., 255 d with
+    255 d = the group's largest scale.  Every restored scale is within d / 2 of
+    the exact absmax (plus the fp32 roundings of d and of the quotient), the
+    largest block of each group gets 255, and the error is far below E4M3's
+    (8 even steps against 3 mantissa bits)."""
+    cfg = si.custom(N=64 * 3, K=192, M=1, r=8, outlier_frac=0.01, seed=3)   # 576 blocks
+    W = si.weight(cfg, 0)
+    codes, qs, ds, am = orc.quantize(W, "nf4", dq_format="uint8")
+    codes_e, qs_e, ds_e, _ = orc.quantize(W, "nf4", dq_format="e4m3")
+    assert np.array_equal(codes, codes_e)           # the codes use the exact absmax either way
+    nb = W.size // 64
+    assert qs.size == nb and ds.size == 3
+    rest = _uint8_restored(qs, ds)
+    a = am.astype(np.float64)
+    d = np.repeat(ds.astype(np.float64), 256)[:nb]
+    assert np.all(np.abs(rest - a) <= d * (0.5 + 2.0 ** -16))
+    for g in range(3):
+        b0, b1 = 256 * g, min(256 * g + 256, nb)
+        top = b0 + int(np.argmax(am[b0:b1]))
+        assert qs[top] == 255
+        assert abs(rest[top] - a[top]) <= a[top] * 2.0 ** -22
+    # on Gaussian weights without outliers the block scales sit near the group
+    # maximum, where the even grid's step (max / 255) beats E4M3's 2^-4
+    Wg = si.weight(si.custom(N=64 * 3, K=192, M=1, r=8, seed=4), 0)
+    _, qg, dg, ag = orc.quantize(Wg, "nf4", dq_format="uint8")
+    _, qe, de, _ = orc.quantize(Wg, "nf4", dq_format="e4m3")
+    ag = ag.astype(np.float64)
+    rest_e = np.array([orc.e4m3_value(int(q)) for q in qe]) * np.repeat(de.astype(np.float64), 256)[:nb]
+    rel_u8 = np.sqrt(np.mean(((_uint8_restored(qg, dg) - ag) / ag) ** 2))
+    rel_e4 = np.sqrt(np.mean(((rest_e - ag) / ag) ** 2))
+    assert rel_u8 < 0.25 * rel_e4
+
+
+def test_uint8_double_quant_exact_on_a_grid_and_ties_to_even(orc):
+    """Scales on the grid k 2^-10 with the group maximum 255 * 2^-10 make
+    d = 2^-10 exactly, so each code is k itself and the restored scale is
+    exact; scales halfway between grid points, (k + 1/2) 2^-10, go to the even
+    neighbour (round half to even)."""
+    ks = [255, 0, 1, 2, 3, 17, 128, 254, 77, 200]
+    halves = [0.5, 1.5, 2.5, 100.5, 253.5]
+    targets = [k * 2.0 ** -10 for k in ks] + [h * 2.0 ** -10 for h in halves]
+    W = np.zeros((len(targets), 64), np.float32)
+    for i, t in enumerate(targets):
+        W[i, 5] = np.float32(-t if i % 2 else t)     # the block absmax is |W[i, 5]|
+    codes, qs, ds, am = orc.quantize(W, "nf4", dq_format="uint8")
+    assert ds[0] == np.float32(2.0 ** -10)
+    assert list(qs[:len(ks)]) == ks
+    assert list(qs[len(ks):]) == [0, 2, 2, 100, 254]
+    rest = _uint8_restored(qs, ds)
+    assert np.array_equal(rest[:len(ks)], np.array(ks, np.float64) * 2.0 ** -10)
+    # an all-zero group: d = 0 and every code 0
+    c0, q0, d0, _ = orc.quantize(np.zeros((4, 64), np.float32), "nf4", dq_format="uint8")
+    assert d0[0] == 0.0 and not q0.any()
+
+
+def test_uint8_dequantize_uses_q_times_d(orc):
+    """Dequantized weights of the uint8 format equal those of the fp32-scale
+    format whose block scales are q_b * d_g rounded once to fp32 (numpy's
+    double -> float rounding): the two scale decodes agree."""
+    cfg = si.custom(N=32, K=256, M=1, r=8, seed=8)
+    W = si.weight(cfg, 0)
+    codes, qs, ds, am = orc.quantize(W, "nf4", dq_format="uint8")
+    sc = _uint8_restored(qs, ds).astype(np.float32)
+    got = orc.dequantize(codes, qs, ds, *W.shape, dq_format="uint8")
+    want = orc.dequantize(codes, None, sc, *W.shape)
+    assert np.array_equal(got, want)
+
+
 def test_storage_footprint_closed_forms(orc):
     """Ultralytics "QLoRA" and vnread "Grokking QLoRA": 0.5 -> ~0.127 bits/param,
     ~0.37 saved, ~3 GB at 65B, ~130 GB at 16 bit, NF4 ~33 GB, NF4+DQ ~34 GB."""
@@ -581,8 +656,9 @@ def test_int4_nearest_level_matches_exact_rational_rule(orc):
 
 
 @pytest.mark.parametrize("codebook", ["nf4", "int4"])
-@pytest.mark.parametrize("dq", [True, False])
-def test_variant_dequant_error_bound_and_self_codes(orc, codebook, dq):
+@pytest.mark.parametrize("dq,fmt", [(True, "e4m3"), (True, "uint8"), (False, "e4m3")],
+                         ids=["e4m3", "uint8", "fp32"])
+def test_variant_dequant_error_bound_and_self_codes(orc, codebook, dq, fmt):
     """For every codebook and scale format: |w' - w| <= half the largest level gap
     times the block absmax, plus the scale's own error, plus half a bf16 ulp; a
     block holding the levels times 2^e comes back as bf16 of the levels times 2^e
@@ -591,10 +667,13 @@ def test_variant_dequant_error_bound_and_self_codes(orc, codebook, dq):
     L = orc.codebook_levels(codebook).astype(np.float64)
     cfg = si.custom(N=96, K=256, M=1, r=8, seed=9, outlier_frac=0.01)
     W = si.weight(cfg, 0)
-    codes, qs, ds, am = orc.quantize(W, codebook, double_quant=dq)
-    deq = si.bf16_bits_to_f32(orc.dequantize(codes, qs, ds, *W.shape, codebook=codebook)).astype(np.float64)
+    codes, qs, ds, am = orc.quantize(W, codebook, double_quant=dq, dq_format=fmt)
+    deq = si.bf16_bits_to_f32(orc.dequantize(codes, qs, ds, *W.shape, codebook=codebook,
+                                             dq_format=fmt)).astype(np.float64)
     a = np.repeat(am.astype(np.float64), 64).reshape(W.shape)
-    if dq:
+    if dq and fmt == "uint8":
+        sc = np.repeat(_uint8_restored(qs, ds), 64).reshape(W.shape)
+    elif dq:
         sc = np.repeat(np.array([orc.e4m3_value(int(q)) for q in qs]) *
                        np.repeat(ds.astype(np.float64), 256)[:qs.size], 64).reshape(W.shape)
     else:
@@ -605,8 +684,8 @@ def test_variant_dequant_error_bound_and_self_codes(orc, codebook, dq):
     Lf = orc.codebook_levels(codebook)
     for e in (-9, 0, 4):
         blk = (np.tile(Lf, 4) * np.float32(2.0 ** e)).astype(np.float32).reshape(1, 64)
-        c2, q2, d2, _ = orc.quantize(blk, codebook, double_quant=dq)
-        got = orc.dequantize(c2, q2, d2, 1, 64, codebook=codebook)
+        c2, q2, d2, _ = orc.quantize(blk, codebook, double_quant=dq, dq_format=fmt)
+        got = orc.dequantize(c2, q2, d2, 1, 64, codebook=codebook, dq_format=fmt)
         want = torch.from_numpy(blk).bfloat16().view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got, want), (codebook, dq, e)
 
