@@ -25,6 +25,9 @@ QL_DTYPE_BF16 = 1
 QL_CODEBOOK_NF4 = 0
 QL_CODEBOOK_INT4 = 1
 CODEBOOKS = {"nf4": QL_CODEBOOK_NF4, "int4": QL_CODEBOOK_INT4}
+QL_DQ_E4M3 = 0
+QL_DQ_UINT8 = 1
+DQ_FORMATS = {"e4m3": QL_DQ_E4M3, "uint8": QL_DQ_UINT8}
 QL_DUAL_SEPARATE = 1
 QL_DUAL_SWIGLU = 2
 QLORA_MAX_RANK = 128
@@ -49,7 +52,8 @@ class _AdamwTensor(ctypes.Structure):
 class _Weight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
                 ("dscale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
-                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32), ("codebook", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32), ("codebook", ctypes.c_int32),
+                ("dq_format", ctypes.c_int32)]
 
 
 def lib() -> ctypes.CDLL:
@@ -69,7 +73,7 @@ def lib() -> ctypes.CDLL:
     L.nf4_storage_bytes.restype = I
     L.nf4_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P, P]
     L.nf4_quantize.restype = I
-    L.qlora_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P, P]
+    L.qlora_quantize.argtypes = [P, I64, I64, I, I, I, P, P, P, P, P]
     L.qlora_quantize.restype = I
     L.qlora_codebook_levels.argtypes = [I, P]
     L.qlora_codebook_levels.restype = I
@@ -155,14 +159,16 @@ def nf4_storage_bytes(rows: int, cols: int, block: int = 64, dq_block: int = 256
 @dataclasses.dataclass
 class NF4Weight:
     """A quantized frozen weight [rows][cols] held in device tensors.  With
-    double_quant the block scales are E4M3 bytes in qscale and group constants
-    in dscale; without, qscale is None and dscale holds the fp32 block scales."""
+    double_quant the block scales are 8-bit codes in qscale (dq_format "e4m3" or
+    "uint8") and group constants in dscale; without, qscale is None and dscale
+    holds the fp32 block scales."""
     codes: "torch.Tensor"              # uint8 [rows*cols/2]
     qscale: Optional["torch.Tensor"]   # uint8 [rows*cols/64], or None
     dscale: "torch.Tensor"             # float32 [ceil(nb/256)], or [nb]
     rows: int
     cols: int
     codebook: str = "nf4"
+    dq_format: str = "e4m3"
 
     @property
     def double_quant(self) -> bool:
@@ -175,6 +181,8 @@ class NF4Weight:
         import torch
         if self.codebook not in CODEBOOKS:
             raise ValueError(f"unknown codebook {self.codebook!r}")
+        if self.dq_format not in DQ_FORMATS:
+            raise ValueError(f"unknown dq_format {self.dq_format!r}")
         c, q, d = nf4_storage_bytes(self.rows, self.cols, 64, 256 if self.double_quant else 0)
         _need(self.codes, torch.uint8, (c,), "codes")
         if self.qscale is not None:
@@ -188,30 +196,36 @@ class NF4Weight:
         self.validate()
         return _Weight(self.codes.data_ptr(), _ptr(self.qscale), self.dscale.data_ptr(),
                        self.rows, self.cols, 64, 256 if self.double_quant else 0,
-                       CODEBOOKS[self.codebook])
+                       CODEBOOKS[self.codebook], DQ_FORMATS[self.dq_format])
 
     @staticmethod
     def empty(rows: int, cols: int, device="cuda", codebook: str = "nf4",
-              double_quant: bool = True) -> "NF4Weight":
+              double_quant: bool = True, dq_format: str = "e4m3") -> "NF4Weight":
         import torch
         c, q, d = nf4_storage_bytes(rows, cols, 64, 256 if double_quant else 0)
         return NF4Weight(torch.empty(c, dtype=torch.uint8, device=device),
                          torch.empty(q, dtype=torch.uint8, device=device) if double_quant else None,
-                         torch.empty(d // 4, dtype=torch.float32, device=device), rows, cols, codebook)
+                         torch.empty(d // 4, dtype=torch.float32, device=device), rows, cols, codebook,
+                         dq_format)
 
 
 def nf4_quantize(W, out: Optional[NF4Weight] = None, absmax=None, stream=None,
-                 codebook: str = "nf4", double_quant: bool = True) -> NF4Weight:
+                 codebook: str = "nf4", double_quant: bool = True,
+                 dq_format: str = "e4m3") -> NF4Weight:
     """Quantize a cuda fp32 [rows, cols] weight with a codebook ("nf4" or "int4"),
-    with double-quantized scales (default) or fp32 block scales.  ``absmax``
-    (optional cuda fp32 [rows*cols/64]) receives the exact block scales."""
+    with double-quantized scales (default; dq_format "e4m3" or "uint8") or fp32
+    block scales.  ``absmax`` (optional cuda fp32 [rows*cols/64]) receives the
+    exact block scales."""
     import torch
     rows, cols = W.shape
     _need(W, torch.float32, (rows, cols), "W")
+    if dq_format not in DQ_FORMATS:
+        raise ValueError(f"unknown dq_format {dq_format!r}")
     if out is None:
-        out = NF4Weight.empty(rows, cols, W.device, codebook, double_quant)
+        out = NF4Weight.empty(rows, cols, W.device, codebook, double_quant, dq_format)
     w = out
-    if w.codebook != codebook or w.double_quant != double_quant:
+    if w.codebook != codebook or w.double_quant != double_quant or \
+            (double_quant and w.dq_format != dq_format):
         raise ValueError("out has another codebook or scale format")
     if (w.rows, w.cols) != (rows, cols):
         raise ValueError(f"out holds a {w.rows}x{w.cols} weight, W is {rows}x{cols}")
@@ -219,7 +233,8 @@ def nf4_quantize(W, out: Optional[NF4Weight] = None, absmax=None, stream=None,
     if absmax is not None:
         _need(absmax, torch.float32, (rows * cols // 64,), "absmax")
     _check(lib().qlora_quantize(W.data_ptr(), rows, cols, CODEBOOKS[codebook],
-                                256 if double_quant else 0, w.codes.data_ptr(), _ptr(w.qscale),
+                                256 if double_quant else 0, DQ_FORMATS[dq_format],
+                                w.codes.data_ptr(), _ptr(w.qscale),
                                 w.dscale.data_ptr(), _ptr(absmax), _stream(stream)))
     return w
 

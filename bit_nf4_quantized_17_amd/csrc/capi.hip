@@ -61,6 +61,8 @@ int check_weight(const qlora_nf4_weight* w) {
                 w->block, w->dq_block);
   if (w->codebook != QL_CODEBOOK_NF4 && w->codebook != QL_CODEBOOK_INT4)
     return fail(QL_ERR_UNSUPPORTED, "codebook=%d", w->codebook);
+  if (w->dq_format != QL_DQ_E4M3 && w->dq_format != QL_DQ_UINT8)
+    return fail(QL_ERR_UNSUPPORTED, "dq_format=%d (QL_DQ_E4M3 or QL_DQ_UINT8)", w->dq_format);
   if (!w->codes || (w->dq_block && !w->qscale) || !w->dscale)
     return fail(QL_ERR_NULL, "weight buffer is NULL");
   if (w->rows <= 0 || w->cols <= 0 || w->cols % 64)
@@ -76,6 +78,7 @@ NF4View view(const qlora_nf4_weight* w) {
   v.codes = w->codes;
   v.qscale = w->dq_block ? w->qscale : nullptr;
   v.fp32_scale = w->dq_block == 0;
+  v.u8_scale = w->dq_block != 0 && w->dq_format == QL_DQ_UINT8;
   const uint32_t* bits = codebook_bits(w->codebook);
   for (int i = 0; i < 16; ++i) std::memcpy(&v.lv[i], &bits[i], 4);
   v.dscale = w->dscale;
@@ -244,9 +247,12 @@ int nf4_storage_bytes(int64_t rows, int64_t cols, int block, int dq_block, size_
 }
 
 int qlora_quantize(const float* W, int64_t rows, int64_t cols, int codebook, int dq_block,
-                   uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out, void* stream) {
+                   int dq_format, uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
+                   void* stream) {
   if (dq_block != 256 && dq_block != 0)
     return fail(QL_ERR_UNSUPPORTED, "dq_block=%d (256, or 0 for fp32 scales)", dq_block);
+  if (dq_format != QL_DQ_E4M3 && dq_format != QL_DQ_UINT8)
+    return fail(QL_ERR_UNSUPPORTED, "dq_format=%d (QL_DQ_E4M3 or QL_DQ_UINT8)", dq_format);
   if (codebook != QL_CODEBOOK_NF4 && codebook != QL_CODEBOOK_INT4)
     return fail(QL_ERR_UNSUPPORTED, "codebook=%d", codebook);
   if (!W || !codes || (dq_block && !qscale) || !dscale) return fail(QL_ERR_NULL, "a required pointer is NULL");
@@ -257,7 +263,8 @@ int qlora_quantize(const float* W, int64_t rows, int64_t cols, int codebook, int
   if (!aligned16(W) || !aligned16(codes) || (dq_block && !aligned16(qscale)) || !aligned16(dscale) ||
       (absmax_out && !aligned16(absmax_out)))
     return fail(QL_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  return hip_status(launch_quantize(W, rows, cols, codebook, dq_block == 0, codes, qscale, dscale,
+  const int fmt = dq_block == 0 ? SCALE_FP32 : dq_format == QL_DQ_UINT8 ? SCALE_U8 : SCALE_E4M3;
+  return hip_status(launch_quantize(W, rows, cols, codebook, fmt, codes, qscale, dscale,
                                     absmax_out, (hipStream_t)stream),
                     "qlora_quantize launch");
 }
@@ -267,7 +274,7 @@ int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_b
   if (block != 64 || (dq_block != 256 && dq_block != 0))
     return fail(QL_ERR_UNSUPPORTED, "block=%d dq_block=%d (block 64; dq_block 256, or 0 for fp32 scales)",
                 block, dq_block);
-  return qlora_quantize(W, rows, cols, QL_CODEBOOK_NF4, dq_block, codes, qscale, dscale, absmax_out,
+  return qlora_quantize(W, rows, cols, QL_CODEBOOK_NF4, dq_block, QL_DQ_E4M3, codes, qscale, dscale, absmax_out,
                         stream);
 }
 

@@ -60,16 +60,24 @@ inline const uint32_t* codebook_bits(int codebook) {
 
 // A quantized weight as the kernels see it.  With fp32_scale the block
 // scales are the exact fp32 absmax values in dscale[b] (no double
-// quantization, qscale unused); otherwise s_b = fl32(E4M3(qscale[b]) *
-// dscale[b / 256]).  lv holds the codebook's 16 levels.
+// quantization, qscale unused); otherwise s_b = fl32(v(qscale[b]) *
+// dscale[b / 256]) with v the E4M3 value of the byte, or (u8_scale) the
+// byte as an integer.  lv holds the codebook's 16 levels.
 struct NF4View {
   const uint8_t* codes;
   const uint8_t* qscale;
   const float* dscale;
   int64_t N, K;
   bool fp32_scale;
+  bool u8_scale;
   float lv[16];
 };
+
+// Second-level formats of the block scales (kernels' compile-time modes).
+enum ScaleFmt { SCALE_E4M3 = 0, SCALE_FP32 = 1, SCALE_U8 = 2 };
+inline int scale_fmt(const NF4View& w) {
+  return w.fp32_scale ? SCALE_FP32 : w.u8_scale ? SCALE_U8 : SCALE_E4M3;
+}
 
 // The kernels restore a block scale as fl32(E4M3(q) * d) everywhere.  For
 // fp32 scales they read q from an empty buffer (0) and OR in the E4M3 code of
@@ -92,8 +100,10 @@ struct EncodeCuts {
 };
 const EncodeCuts& encode_cuts(int codebook);
 
-// fp32_scale: dscale receives the nb fp32 block scales (qscale unused)
-hipError_t launch_quantize(const float* W, int64_t N, int64_t K, int codebook, bool fp32_scale,
+// fmt (ScaleFmt): SCALE_FP32 -- dscale receives the nb fp32 block scales
+// (qscale unused); SCALE_E4M3 / SCALE_U8 -- 8-bit scales in qscale and one
+// group constant per 256 blocks in dscale
+hipError_t launch_quantize(const float* W, int64_t N, int64_t K, int codebook, int fmt,
                            uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax,
                            hipStream_t s);
 hipError_t launch_dequantize(const NF4View& w, u16* out, hipStream_t s);

@@ -12,7 +12,8 @@
 // -> one bf16 pair), with one copy per lane so that lookups never share a
 // bank; each 64-code block is one pair of v_mfma_f32_16x16x32_bf16 into a
 // fresh accumulator, which is then scaled by the block's restored scale
-// s_b = fl32(E4M3(q) * d) and added in fp32.  (The prefill and training
+// s_b = fl32(v(q) * d) (v: the E4M3 value of the scale byte, or the byte
+// as an integer for uint8-linear scales) and added in fp32.  (The prefill and training
 // kernels multiply the exactly dequantized bf16 weight instead; both round
 // the weight's relative value once to bf16 precision.)
 //
@@ -76,6 +77,7 @@ struct DecArgs {
   uint32_t N, K;
   float lv[16];                             // the codebook's levels
   const float* tpart; int S;                // T partials [S][16][16 RT]
+  int u8;                                   // scale bytes are integers (uint8-linear), not E4M3
   const u16* B; int r; float s;
   u16* Y; float* T_save;
 };
@@ -356,8 +358,10 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       const uint32_t kb_sw = 256u - ((qoff + 16u * (uint32_t)t * nbk) & 255u);
       const float2 dd = *reinterpret_cast<const float2*>(dtab + 2 * (16 * t + i16));
       const uint32_t q = *reinterpret_cast<const uint16_t*>(qtab + (uint32_t)(16 * t + i16) * nbk + kb);
-      const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)q, 0) * (kb < kb_sw ? dd.x : dd.y);
-      const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)q, 1) * (kb + 1u < kb_sw ? dd.x : dd.y);
+      const float v0 = p.u8 ? (float)(q & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 0);
+      const float v1 = p.u8 ? (float)((q >> 8) & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 1);
+      const float s0 = v0 * (kb < kb_sw ? dd.x : dd.y);
+      const float s1 = v1 * (kb + 1u < kb_sw ? dd.x : dd.y);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[t][e] += s0 * t0[e] + s1 * t1[e];
     }
@@ -501,6 +505,7 @@ hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A
   p.N = (uint32_t)w.N; p.K = (uint32_t)w.K;
   for (int i = 0; i < 16; ++i) p.lv[i] = w.lv[i];
   p.tpart = ws; p.S = S;
+  p.u8 = w.u8_scale ? 1 : 0;
   p.B = B; p.r = r; p.s = s;
   p.Y = Y; p.T_save = T_save;
   const unsigned grid = (unsigned)((w.N + 16 * pl.TR - 1) / (16 * pl.TR));

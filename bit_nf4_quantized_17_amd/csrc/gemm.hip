@@ -297,7 +297,8 @@ __device__ __forceinline__ void dequant32(const uint4& c, float sc, const float*
 
 // restored block scale: fl32(E4M3(q) * d), or the stored fp32 scale
 __device__ __forceinline__ float block_scale(const NF4View& w, int64_t blk) {
-  return w.fp32_scale ? w.dscale[blk] : e4m3_decode(w.qscale[blk]) * w.dscale[blk >> 8];
+  return w.fp32_scale ? w.dscale[blk]
+                      : (w.u8_scale ? (float)w.qscale[blk] : e4m3_decode(w.qscale[blk])) * w.dscale[blk >> 8];
 }
 
 // NF4 weight, rows j = n (128 of them), contraction c = k (one 64-block):

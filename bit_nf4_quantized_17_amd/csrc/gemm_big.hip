@@ -170,7 +170,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 struct Bufs {
   __amdgpu_buffer_rsrc_t a, codes, qscale, dscale;
-  uint32_t qor, dshift;   // scale format: E4M3 code OR-ed in, group shift of dscale
+  uint32_t qor, dshift;   // scale format: E4M3 code OR-ed in (QOR_U8: integer scales), group shift of dscale
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -207,9 +207,13 @@ __device__ __forceinline__ void load_w(StageW& st, const Bufs& b, uint32_t n, ui
 }
 
 // fl32(E4M3(q) * d); with fp32 scales q reads 0 from an empty buffer and the
-// OR makes it E4M3(1.0), so the product is the stored scale exactly
+// OR makes it E4M3(1.0), so the product is the stored scale exactly; with
+// uint8-linear scales (qor == QOR_U8) fl32(q * d)
+constexpr uint32_t QOR_U8 = 0x100u;
 __device__ __forceinline__ float stage_scale(const StageW& st, uint32_t qor) {
-  return __builtin_amdgcn_cvt_f32_fp8((int)(st.q | qor), 0) * st.d;
+  const float v = qor == QOR_U8 ? (float)(st.q & 0xFFu)
+                                : __builtin_amdgcn_cvt_f32_fp8((int)(st.q | qor), 0);
+  return v * st.d;
 }
 
 __device__ __forceinline__ void store_a(const StageA& st, u16* sA, int tid) {
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   bf.qscale = rsrc(wv.qscale, wv.fp32_scale ? 0u : (uint32_t)(wv.N * wv.K / 64));
   bf.dscale = rsrc(wv.dscale, (uint32_t)(4 * (wv.fp32_scale ? wv.N * wv.K / 64
                                                              : (wv.N * wv.K / 64 + 255) / 256)));
-  bf.qor = wv.fp32_scale ? 0x38u : 0u;   // E4M3 code of 1.0
+  bf.qor = wv.fp32_scale ? 0x38u : wv.u8_scale ? QOR_U8 : 0u;   // 0x38: E4M3 code of 1.0
   bf.dshift = wv.fp32_scale ? 0u : 8u;
   // this lane's half of the block table: levels 8p .. 8p + 7 for lane parity p
   const bool odd_lane = tid & 1;

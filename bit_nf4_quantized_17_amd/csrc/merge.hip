@@ -44,7 +44,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 struct MergeArgs {
   const uint8_t* codes; const uint8_t* qscale; const float* dscale;   // merge: the NF4 base
-  bool fp32_scale; float lv[16];                                      // its scale format, codebook
+  bool fp32_scale, u8_scale; float lv[16];                            // its scale format, codebook
   const u16* w_in;                                                    // unmerge: the bf16 base
   int64_t N, K;
   const u16* A; const u16* B; int r; float s;                         // s already carries the sign
@@ -235,7 +235,8 @@ __global__ __launch_bounds__(NTHREADS) void k_merge(MergeArgs p) {
         }
       } else {
         // W' = bf16(L[code] * fl32(E4M3(q) * d)), element e in nibble e
-        const float sb = e4m3_decode((qb[h][i] | (p.fp32_scale ? 0x38u : 0u)) & 127u) * dg[h][i];
+        const float sb = (p.u8_scale ? (float)qb[h][i] : e4m3_decode((qb[h][i] | (p.fp32_scale ? 0x38u : 0u)) & 127u)) *
+                         dg[h][i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) base[e] = bf16_to_f32(f32_to_bf16(levels[(cw[h][i] >> (4 * e)) & 15u] * sb));
       }
@@ -271,6 +272,7 @@ hipError_t launch_merge(const NF4View& w, const u16* A, const u16* B, int r, flo
   mrg::MergeArgs p{};
   p.codes = w.codes; p.qscale = w.qscale; p.dscale = w.dscale;
   p.fp32_scale = w.fp32_scale;
+  p.u8_scale = w.u8_scale;
   for (int i = 0; i < 16; ++i) p.lv[i] = w.lv[i];
   p.N = w.N; p.K = w.K; p.A = A; p.B = B; p.r = r; p.s = s; p.out = out;
   return mrg::launch<false>(p, st);

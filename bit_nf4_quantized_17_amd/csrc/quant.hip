@@ -1,6 +1,8 @@
 // quant.hip -- NF4 quantization (absmax per 64, nearest-level encode, pack,
 // double quantization of the scales to E4M3 per 256 blocks) and streaming
-// dequantization to bf16.
+// dequantization to bf16.  The second level of the scales is E4M3 (vnread)
+// or, in the uint8-linear reading of the Ultralytics bullet ("8 bits"), an
+// integer grid 0 .. 255 times max / 255; or the scales stay fp32.
 //
 // Method: Ultralytics glossary "QLoRA", "How QLoRA works" (NF4 bullet, double
 // quantization bullet, the encoding snippet); vnread "Grokking QLoRA",
@@ -89,7 +91,7 @@ __device__ __forceinline__ int bin_of(float q) {
   return min(max(b, 0), QBINS - 1);
 }
 
-template <bool FP32>
+template <int FMT>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ qscale,
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                 reinterpret_cast<u32x4_t*>(codes + b0 * 32) + i);
 
   const float a_t = tid < nbg ? s_amax[tid] : 0.0f;
-  if constexpr (FP32) {  // the scales themselves, no double quantization
+  if constexpr (FMT == SCALE_FP32) {  // the scales themselves, no double quantization
     if (tid < nbg) dscale[b0 + tid] = a_t;
     return;
   }
@@ -196,9 +198,17 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   if (lane == 0) s_wmax[wave] = wm;
   __syncthreads();
   const float c = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
-  const float d = c / 448.0f;
-  if (tid == 0) dscale[g] = d;
-  reinterpret_cast<uint8_t*>(s_q)[tid] = (uint8_t)(d == 0.0f ? 0u : e4m3_encode(a_t / d));
+  if constexpr (FMT == SCALE_U8) {
+    // uint8-linear: the nearest of 0, d, ..., 255 d with d = max / 255
+    // (the quotient rounded half to even; IEEE division)
+    const float d = c / 255.0f;
+    if (tid == 0) dscale[g] = d;
+    reinterpret_cast<uint8_t*>(s_q)[tid] = (uint8_t)(d == 0.0f ? 0u : (uint32_t)fminf(rintf(a_t / d), 255.0f));
+  } else {
+    const float d = c / 448.0f;
+    if (tid == 0) dscale[g] = d;
+    reinterpret_cast<uint8_t*>(s_q)[tid] = (uint8_t)(d == 0.0f ? 0u : e4m3_encode(a_t / d));
+  }
   __syncthreads();
   if (nbg == 256) {
     if (tid < 16)
@@ -209,22 +219,26 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   }
 }
 
-hipError_t launch_quantize(const float* W, int64_t N, int64_t K, int codebook, bool fp32_scale,
+hipError_t launch_quantize(const float* W, int64_t N, int64_t K, int codebook, int fmt,
                            uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax,
                            hipStream_t s) {
   const int64_t nb = N * K / 64;
   const int64_t ng = (nb + 255) / 256;
-  if (fp32_scale)
-    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
+  if (fmt == SCALE_FP32)
+    hipLaunchKernelGGL(k_quantize<SCALE_FP32>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
+                       dscale, absmax, encode_cuts(codebook));
+  else if (fmt == SCALE_U8)
+    hipLaunchKernelGGL(k_quantize<SCALE_U8>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
                        dscale, absmax, encode_cuts(codebook));
   else
-    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
+    hipLaunchKernelGGL(k_quantize<SCALE_E4M3>, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codes, qscale,
                        dscale, absmax, encode_cuts(codebook));
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: w' = bf16_RNE(fl32(L[code] * fl32(E4M3(q) * d))).  One
+// Dequantize: w' = bf16_RNE(fl32(L[code] * fl32(v(q) * d))), v the E4M3
+// value of the scale byte or (uint8-linear) the byte itself.  One
 // workgroup (4 waves) per group of 256 blocks, so d is one scalar load; wave w
 // writes its own contiguous 64 blocks (8 KiB of bf16).  In step j a lane takes
 // 8 codes of block 8j + lane/8 (one 4-byte load) and writes their 8 bf16 values
@@ -237,7 +251,7 @@ constexpr int DQ_STEPS = 8;  // 8 blocks per wave and step
 
 struct Levels { float v[16]; };
 
-template <bool FP32>
+template <int FMT>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ qscale,
                                                     const float* __restrict__ dscale,
@@ -250,6 +264,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   const int64_t b0 = g * 256 + wave * 64;               // first block of this wave
   const int64_t nbw = min<int64_t>(64, nblocks - b0);  // its blocks (<= 0 past the end)
   if (tid < 16) s_L[tid] = lv.v[tid];
+  constexpr bool FP32 = FMT == SCALE_FP32;
   const float d = FP32 ? 0.0f : dscale[g];
   uint32_t c[DQ_STEPS], qv[DQ_STEPS];
   float sv[DQ_STEPS];
@@ -271,7 +286,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 #pragma unroll
   for (int j = 0; j < DQ_STEPS; ++j) {
     const int blk = j * 8 + (lane >> 3);
-    const float sc = FP32 ? sv[j] : e4m3_decode(qv[j]) * d;
+    const float sc = FP32 ? sv[j] : (FMT == SCALE_U8 ? (float)qv[j] : e4m3_decode(qv[j])) * d;
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -289,11 +304,15 @@ hipError_t launch_dequantize(const NF4View& w, u16* out, hipStream_t s) {
   const int64_t ng = (nb + 255) / 256;
   Levels lv;
   for (int i = 0; i < 16; ++i) lv.v[i] = w.lv[i];
-  if (w.fp32_scale)
-    hipLaunchKernelGGL(k_dequantize<true>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
+  const int fmt = scale_fmt(w);
+  if (fmt == SCALE_FP32)
+    hipLaunchKernelGGL(k_dequantize<SCALE_FP32>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
+                       w.dscale, nb, out, lv);
+  else if (fmt == SCALE_U8)
+    hipLaunchKernelGGL(k_dequantize<SCALE_U8>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
                        w.dscale, nb, out, lv);
   else
-    hipLaunchKernelGGL(k_dequantize<false>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
+    hipLaunchKernelGGL(k_dequantize<SCALE_E4M3>, dim3((unsigned)ng), dim3(256), 0, s, w.codes, w.qscale,
                        w.dscale, nb, out, lv);
   return hipGetLastError();
 }

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define QLORA_ABI_VERSION 2
+#define QLORA_ABI_VERSION 3
 
 typedef enum {
   QL_OK = 0,
@@ -82,24 +82,37 @@ enum { QL_DTYPE_BF16 = 1 };  /* the only compute dtype: bfloat16 operands, fp32 
  * of the Ultralytics "QLoRA" encoding snippet. */
 enum { QL_CODEBOOK_NF4 = 0, QL_CODEBOOK_INT4 = 1 };
 
+/* Second-level (double-quantization) formats of the 8-bit block scales.
+ * The Ultralytics "QLoRA" double-quantization bullet says "8 bits, blocks of
+ * 256"; vnread "Grokking QLoRA", "Double Quantization", names FP8:
+ *  QL_DQ_E4M3  (0): OCP FP8 E4M3; per group d = max / 448, q = E4M3(a / d),
+ *                   restored fl32(E4M3(q) * d).
+ *  QL_DQ_UINT8 (1): the plain integer reading; per group d = fl32(max / 255),
+ *                   q = min(255, round-half-even(fl32(a / d))) (0 if d = 0),
+ *                   restored fl32(q * d). */
+enum { QL_DQ_E4M3 = 0, QL_DQ_UINT8 = 1 };
+
 /* A quantized frozen weight W [rows = N][cols = K] (device pointers).
  *  codes  : N*K/2 bytes; byte e/2 holds flattened element e, even e in the low
  *           nibble; the code indexes the 16 levels of `codebook`.
  *  block  : must be 64 (block b covers flattened elements [64b, 64b+64),
  *           always inside one row because K % 64 == 0); nb = N*K/64.
  *  dq_block = 256 (double quantization, the QLoRA default):
- *    qscale : nb bytes, OCP FP8 E4M3 code of each block's scale, at most
- *             0x7E (448, what nf4_quantize writes; the sign bit and the
- *             E4M3 NaN code 0x7F are not valid scales);
+ *    qscale : nb bytes, the 8-bit code of each block's scale in dq_format:
+ *             an OCP FP8 E4M3 code at most 0x7E (448, what nf4_quantize
+ *             writes; the sign bit and the E4M3 NaN code 0x7F are not valid
+ *             scales), or (QL_DQ_UINT8) an integer 0..255;
  *    dscale : ng = ceil(nb/256) fp32; group g covers blocks [256g, 256g+256)
  *             (the last may be shorter); restored block scale is
- *             fl32(E4M3(qscale[b]) * dscale[b/256]).
+ *             fl32(v(qscale[b]) * dscale[b/256]), v the code's value.
  *  dq_block = 0 (no double quantization; Transformers "Bitsandbytes", 4-bit
  *    section, nested quantization off):
  *    qscale : unused, may be NULL;
  *    dscale : nb fp32, the block scales (each block's exact absmax).
  *  codebook: QL_CODEBOOK_NF4 (0, the default of a zero-initialised
- *    descriptor) or QL_CODEBOOK_INT4. */
+ *    descriptor) or QL_CODEBOOK_INT4.
+ *  dq_format: QL_DQ_E4M3 (0, the default) or QL_DQ_UINT8; read only when
+ *    dq_block = 256. */
 typedef struct {
   const uint8_t* codes;
   const uint8_t* qscale;
@@ -107,6 +120,7 @@ typedef struct {
   int64_t rows, cols;
   int32_t block, dq_block;
   int32_t codebook;
+  int32_t dq_format;
 } qlora_nf4_weight;
 
 /* ABI version (QLORA_ABI_VERSION of the built library). */
@@ -152,17 +166,21 @@ int nf4_quantize(const float* W, int64_t rows, int64_t cols, int block, int dq_b
                  void* stream);
 
 /* Quantize with a codebook (QL_CODEBOOK_NF4 or QL_CODEBOOK_INT4) and a scale
- * format (dq_block 256: double-quantized E4M3 scales; 0: fp32 block scales
- * in dscale [nb], qscale unused).  Same rule as nf4_quantize with the
- * codebook's levels; an all-zero block gets the code of v = 0 (the nearest
- * level, the lower on a tie: 7 for both codebooks). */
+ * format: dq_block 256 with dq_format QL_DQ_E4M3 (as nf4_quantize) or
+ * QL_DQ_UINT8 (d_g = fl32(max_{b in g} a_b / 255), q_b = min(255,
+ * round-half-even(fl32(a_b / d_g))), 0 when d_g == 0); dq_block 0: fp32 block
+ * scales in dscale [nb], qscale unused (dq_format ignored).  Same encode rule
+ * as nf4_quantize with the codebook's levels; an all-zero block gets the code
+ * of v = 0 (the nearest level, the lower on a tie: 7 for both codebooks).
+ * QL_ERR_UNSUPPORTED for an unknown codebook, dq_block or dq_format. */
 int qlora_quantize(const float* W, int64_t rows, int64_t cols, int codebook, int dq_block,
-                   uint8_t* codes, uint8_t* qscale, float* dscale, float* absmax_out,
-                   void* stream);
+                   int dq_format, uint8_t* codes, uint8_t* qscale, float* dscale,
+                   float* absmax_out, void* stream);
 
 /* Dequantize to bfloat16: W_bf16[e] = bf16_RNE(fl32(L[code_e] * s_b)) with the
- * restored block scale s_b = fl32(E4M3(q_b) * d_g) (or the fp32 dscale[b]
- * when dq_block is 0) and L the weight's codebook.  Transformers docs
+ * restored block scale s_b = fl32(v(q_b) * d_g), v the E4M3 value or (for
+ * QL_DQ_UINT8) the integer of the scale byte (or the fp32 dscale[b] when
+ * dq_block is 0) and L the weight's codebook.  Transformers docs
  * "Bitsandbytes", section on dequantizing a model to its original precision;
  * Ultralytics "QLoRA" (restore = level times block scale).
  * W_bf16: device, rows*cols uint16 (bf16 bits). */

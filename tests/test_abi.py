@@ -234,10 +234,15 @@ def test_codebooks_and_scale_formats_are_validated():
     assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == -1
     w = _weight(dq=0, qs=None)
     assert L.nf4_dequantize(ctypes.byref(w), FAKE + 4, None) == -4     # got past the weight checks
-    assert L.qlora_quantize(FAKE, 64, 64, 3, 256, FAKE, FAKE, FAKE, None, None) == -3
-    assert L.qlora_quantize(FAKE, 64, 64, 1, 64, FAKE, FAKE, FAKE, None, None) == -3
-    assert L.qlora_quantize(FAKE, 64, 64, 1, 256, FAKE, None, FAKE, None, None) == -1
-    assert L.qlora_quantize(FAKE, 64, 64, 1, 0, FAKE, None, FAKE + 4, None, None) == -4
+    w = _weight()
+    w.dq_format = 2
+    assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == -3
+    assert b"dq_format" in L.qlora_last_error()
+    assert L.qlora_quantize(FAKE, 64, 64, 3, 256, 0, FAKE, FAKE, FAKE, None, None) == -3
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 64, 0, FAKE, FAKE, FAKE, None, None) == -3
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 256, 2, FAKE, FAKE, FAKE, None, None) == -3
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 256, 1, FAKE, None, FAKE, None, None) == -1
+    assert L.qlora_quantize(FAKE, 64, 64, 1, 0, 0, FAKE, None, FAKE + 4, None, None) == -4
     assert q.nf4_storage_bytes(128, 256, 64, 0) == (128 * 256 // 2, 0, 4 * 128 * 256 // 64)
     assert q.nf4_storage_bytes(128, 256, 64, 256) == (128 * 256 // 2, 512, 4 * 2)
     lv = q.codebook_levels("int4")

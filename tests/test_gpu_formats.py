@@ -1,9 +1,11 @@
 """GPU parity of the codebook and scale-format variants through the C ABI.
 
-Variants (the NF4 + double-quantized default is covered by test_gpu_parity):
-the INT4 comparison codebook of the Ultralytics "QLoRA" snippet, and block
-scales kept as fp32 (the Transformers "Bitsandbytes" 4-bit configuration
-without nested quantization), alone and combined.  Codes, scales and the
+Variants (the NF4 + E4M3 double-quantized default is covered by
+test_gpu_parity): the INT4 comparison codebook of the Ultralytics "QLoRA"
+snippet; block scales kept as fp32 (the Transformers "Bitsandbytes" 4-bit
+configuration without nested quantization); and the uint8-linear reading of
+the double quantization's "8 bits in blocks of 256" (Ultralytics "QLoRA");
+alone and combined.  Codes, scales and the
 dequantized weight must match the oracle bit for bit; forward, backward,
 decode-size forward, merge and the dual projection are held to the same bars
 as the default format."""
@@ -21,17 +23,18 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import bit_nf4_quantized_17_amd as q  # noqa: E402
 
-FORMATS = [("nf4", False), ("int4", True), ("int4", False)]
-FMT_IDS = ["nf4-fp32scale", "int4-dq", "int4-fp32scale"]
+FORMATS = [("nf4", False, "e4m3"), ("int4", True, "e4m3"), ("int4", False, "e4m3"),
+           ("nf4", True, "uint8"), ("int4", True, "uint8")]
+FMT_IDS = ["nf4-fp32scale", "int4-dq", "int4-fp32scale", "nf4-u8dq", "int4-u8dq"]
 
 
-def _quantize(orc, W, codebook, dq, label):
+def _quantize(orc, W, codebook, dq, label, fmt="e4m3"):
     """GPU quantize + dequantize against the oracle, bit for bit; returns the
     GPU weight and the oracle's dequantized bf16 weight."""
     dW = torch.from_numpy(np.ascontiguousarray(W)).cuda()
     absmax = torch.empty(W.size // 64, dtype=torch.float32, device="cuda")
-    w = q.nf4_quantize(dW, absmax=absmax, codebook=codebook, double_quant=dq)
-    rc, rq, rd, ra = orc.quantize(W, codebook, double_quant=dq)
+    w = q.nf4_quantize(dW, absmax=absmax, codebook=codebook, double_quant=dq, dq_format=fmt)
+    rc, rq, rd, ra = orc.quantize(W, codebook, double_quant=dq, dq_format=fmt)
     assert np.array_equal(w.codes.cpu().numpy(), rc), f"{label}: codes differ"
     assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), f"{label}: absmax"
     assert np.array_equal(w.dscale.cpu().numpy().view(np.uint32), rd.view(np.uint32)), f"{label}: dscale"
@@ -39,21 +42,21 @@ def _quantize(orc, W, codebook, dq, label):
         assert np.array_equal(w.qscale.cpu().numpy(), rq), f"{label}: qscale differs"
     else:
         assert w.qscale is None
-    ref = orc.dequantize(rc, rq, rd, *W.shape, codebook=codebook)
+    ref = orc.dequantize(rc, rq, rd, *W.shape, codebook=codebook, dq_format=fmt)
     assert np.array_equal(tensor_bits(q.nf4_dequantize(w)), ref), f"{label}: dequantized bf16 differs"
     return w, ref
 
 
-@pytest.mark.parametrize("codebook,dq", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("codebook,dq,fmt", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("N,K,outliers", [(300, 256, 0.01), (513, 1088, 0.01), (7, 320, 0.0)])
-def test_quantize_formats_bitwise(orc, codebook, dq, N, K, outliers):
+def test_quantize_formats_bitwise(orc, codebook, dq, fmt, N, K, outliers):
     cfg = si.custom(N=N, K=K, M=1, r=8, outlier_frac=outliers, seed=N + 2 * K)
-    log(f"[quantize {codebook} dq={dq}] {N}x{K}")
-    _quantize(orc, si.weight(cfg, 0), codebook, dq, f"{codebook} dq={dq} {N}x{K}")
+    log(f"[quantize {codebook} dq={dq} {fmt}] {N}x{K}")
+    _quantize(orc, si.weight(cfg, 0), codebook, dq, f"{codebook} dq={dq} {fmt} {N}x{K}", fmt)
 
 
-@pytest.mark.parametrize("codebook,dq", FORMATS, ids=FMT_IDS)
-def test_quantize_formats_zero_blocks_and_ties(orc, codebook, dq):
+@pytest.mark.parametrize("codebook,dq,fmt", FORMATS, ids=FMT_IDS)
+def test_quantize_formats_zero_blocks_and_ties(orc, codebook, dq, fmt):
     """All-zero blocks (two whole groups) take the code of v = 0; values on the
     codebook's decision points and its levels times powers of two."""
     L = orc.codebook_levels(codebook)
@@ -66,7 +69,7 @@ def test_quantize_formats_zero_blocks_and_ties(orc, codebook, dq):
         vals = np.concatenate([L, mids.astype(np.float32), -L[::-1]]).astype(np.float32)
         W[row, :vals.size] = vals * np.float32(2.0 ** e)
         W[row, 64:128] = np.tile(L, 4) * np.float32(2.0 ** (e / 2))
-    _quantize(orc, W, codebook, dq, f"{codebook} dq={dq} edge")
+    _quantize(orc, W, codebook, dq, f"{codebook} dq={dq} {fmt} edge", fmt)
 
 
 SHAPES = [
@@ -78,13 +81,13 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("codebook,dq", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("codebook,dq,fmt", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("N,K,M,r,alpha", SHAPES)
-def test_fwd_bwd_formats(orc, codebook, dq, N, K, M, r, alpha):
+def test_fwd_bwd_formats(orc, codebook, dq, fmt, N, K, M, r, alpha):
     cfg = si.custom(N=N, K=K, M=M, r=r, alpha=alpha, seed=5 * N + K)
-    label = f"{codebook} dq={dq} N={N} K={K} M={M} r={r}"
+    label = f"{codebook} dq={dq} {fmt} N={N} K={K} M={M} r={r}"
     log(f"[fwd/bwd] {label}")
-    w, Wdq = _quantize(orc, si.weight(cfg, 0), codebook, dq, label)
+    w, Wdq = _quantize(orc, si.weight(cfg, 0), codebook, dq, label, fmt)
     X, A, B, dY = si.activations(cfg, 0), *si.adapters(cfg, 0), si.upstream(cfg, 0)
     dXin, dA_in, dB_in, ddY = bf16_tensor(X), bf16_tensor(A), bf16_tensor(B), bf16_tensor(dY)
     Y, T = q.qlora_linear_fwd(w, dXin, dA_in, dB_in, alpha)
@@ -100,15 +103,15 @@ def test_fwd_bwd_formats(orc, codebook, dq, N, K, M, r, alpha):
     assert_close(tensor_f64(dB), dBr, "dB")
 
 
-@pytest.mark.parametrize("codebook,dq", FORMATS, ids=FMT_IDS)
-def test_merge_formats(orc, codebook, dq):
+@pytest.mark.parametrize("codebook,dq,fmt", FORMATS, ids=FMT_IDS)
+def test_merge_formats(orc, codebook, dq, fmt):
     """Merge with a zero B gives the dequantized weight bit for bit; with the
     adapter, every element is within the merge's rounding bound of the exact
     W' + s B A (the bar of test_gpu_merge)."""
     from test_gpu_merge import check_rounded
     N, K, r, alpha = 300, 320, 16, 32.0
     cfg = si.custom(N=N, K=K, M=1, r=r, alpha=alpha, seed=12)
-    w, Wdq = _quantize(orc, si.weight(cfg, 0), codebook, dq, f"merge {codebook} dq={dq}")
+    w, Wdq = _quantize(orc, si.weight(cfg, 0), codebook, dq, f"merge {codebook} dq={dq} {fmt}", fmt)
     A, B = si.adapters(cfg, 0)
     dA_in, dB_in = bf16_tensor(A), bf16_tensor(B)
     Wz = q.qlora_merge(w, dA_in, torch.zeros_like(dB_in), alpha)
@@ -122,15 +125,18 @@ def test_merge_formats(orc, codebook, dq):
     check_rounded(tensor_bits(Wm), orc.lora_merge(Wdq, A, B, alpha), exact, mag, f"merge {codebook} dq={dq}")
 
 
-def test_dual_mixed_formats_match_single_calls(orc):
-    """A dual projection whose gate weight is INT4 with E4M3 scales and whose up
-    weight is NF4 with fp32 scales: each wave decodes its own weight's format,
-    and the outputs equal two single forwards bit for bit."""
+@pytest.mark.parametrize("gate,up", [(("int4", True, "e4m3"), ("nf4", False, "e4m3")),
+                                     (("nf4", True, "uint8"), ("int4", True, "e4m3"))],
+                         ids=["int4e4m3-nf4fp32", "nf4u8-int4e4m3"])
+def test_dual_mixed_formats_match_single_calls(orc, gate, up):
+    """A dual projection whose gate and up weights have different codebooks
+    and scale formats: each wave decodes its own weight's format, and the
+    outputs equal two single forwards bit for bit."""
     N, K, M, r, alpha = 320, 512, 96, 16, 32.0
     cg = si.custom(N=N, K=K, M=M, r=r, alpha=alpha, seed=21)
     cu = si.custom(N=N, K=K, M=M, r=r, alpha=alpha, seed=22)
-    wg, Wg = _quantize(orc, si.weight(cg, 0), "int4", True, "dual gate")
-    wu, Wu = _quantize(orc, si.weight(cu, 0), "nf4", False, "dual up")
+    wg, Wg = _quantize(orc, si.weight(cg, 0), gate[0], gate[1], "dual gate", gate[2])
+    wu, Wu = _quantize(orc, si.weight(cu, 0), up[0], up[1], "dual up", up[2])
     X = si.activations(cg, 0)
     Ag, Bg = si.adapters(cg, 0)
     Au, Bu = si.adapters(cu, 0)
@@ -145,3 +151,19 @@ def test_dual_mixed_formats_match_single_calls(orc):
     assert_close(tensor_f64(Yg), Gr, "Y_gate")
     Ur, _ = orc.qlora_fwd(Wu, X, Au, Bu, alpha)
     assert_close(tensor_f64(Yu), Ur, "Y_up")
+
+
+@pytest.mark.parametrize("fmt", ["uint8", "e4m3"])
+def test_quantize_dq_formats_at_a_workload_size(orc, fmt):
+    """The 7B attention projection's weight (4096 x 4096, N(0, 0.02)) in both
+    8-bit scale formats, bit for bit, with a decode-size forward (M = 4)."""
+    cfg = si.CONFIGS["attn_4096"]
+    W = si.weight(cfg, 0)
+    log(f"[quantize {fmt}] 4096x4096")
+    w, Wdq = _quantize(orc, W, "nf4", True, f"attn7b {fmt}", fmt)
+    X = si.activations(cfg, 0, 4)
+    A, B = si.adapters(cfg, 0)
+    Y, T = q.qlora_linear_fwd(w, bf16_tensor(X), bf16_tensor(A), bf16_tensor(B), cfg.alpha)
+    torch.cuda.synchronize()
+    Yr, Tr = orc.qlora_fwd(Wdq, X, A, B, cfg.alpha)
+    assert_close(tensor_f64(Y), Yr, f"Y {fmt}")
