@@ -12,9 +12,14 @@ of the step (4MNK + 6Mr(N+K) per trained linear, plus the decode forwards;
 dequantization and quantization count no flops) / wall time of the step.
 
 Also reported: the roofline of the dominant kernel (HIP events recorded by
-the library's timing hook around that kernel's launches), the decode-shape
-and quantize bandwidths against HBM, and the CPU oracle timed on a bounded
-sample of the same workload.
+the library's timing hook around that kernel's launches); the decode-shape
+and quantize bandwidths against HBM; the smaller training shapes C1-C3
+(tiny-layer latency, TFLOP/s of the 7B attention projection and of the 7B
+MLP); the dequantize, merge, dual-projection, format-variant and AdamW
+figures; context from the chip itself (a pure MFMA loop with zero and random
+operands, a streaming HBM read, a device copy, the empty-kernel launch
+floor, and the vendor's dense bf16 GEMM on the fused GEMMs' shapes); and the
+CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -101,7 +106,7 @@ class Layer:
         import torch
         import bit_nf4_quantized_17_amd as q
         import synthetic_inputs as si
-        from tests.helpers import bf16_tensor
+        from synthetic_inputs import bf16_tensor
         L = cfg.layers[li]
         self.name, self.N, self.K, self.M, self.r, self.alpha = L.name, L.N, L.K, cfg.M, cfg.r, cfg.alpha
         self.W = torch.from_numpy(si.weight(cfg, li)).cuda()
@@ -178,11 +183,19 @@ def load_traffic(kernel_key: str, src_hash: str):
 # ---------------------------------------------------------------------------
 # decode and quantize bandwidth (cache-defeating rotation over >= 512 MB)
 # ---------------------------------------------------------------------------
-def bench_decode(hip, reps=60):
+def bench_decode(hip, reps=200):
+    """The decode shapes (W 8192x8192 and 28672x8192, M = 1, 4, 16, r = 16), each
+    forward's weight taken in turn from copies that together exceed 512 MB, so
+    the 256 MB Infinity Cache cannot serve it.  kernel_us: HIP events recorded
+    by the library around the forward's launches (the T-partials launch and
+    the weight stream), averaged over `reps` eager calls; graph_us: the same
+    calls captured in one HIP graph and replayed back to back (GPU time per
+    call with no host gaps).  GB/s counts the algorithmic bytes of one call
+    against graph_us."""
     import torch
     import bit_nf4_quantized_17_amd as q
     import synthetic_inputs as si
-    from tests.helpers import bf16_tensor
+    from synthetic_inputs import bf16_tensor
     cfg = si.CONFIGS["decode_8192_28672"]
     out = []
     st = torch.cuda.current_stream().cuda_stream
@@ -200,24 +213,45 @@ def bench_decode(hip, reps=60):
             T = torch.empty(M, cfg.r, dtype=torch.float32, device="cuda")
             ws = torch.empty(max(256, q.qlora_fwd_workspace_bytes(M, L.N, L.K, cfg.r)),
                              dtype=torch.uint8, device="cuda")
-            for i in range(5):
+
+            def call(i):
                 q.qlora_linear_fwd(copies[i % ncopy], X, A, B, cfg.alpha, Y=Y, T=T, workspace=ws)
+            for i in range(5):
+                call(i)
             kev = [(hip.event(), hip.event()) for _ in range(reps)]
-            e0, e1 = hip.event(), hip.event()
             torch.cuda.synchronize()
-            hip.record(e0, st)
             for i in range(reps):
                 q.qlora_set_timing_events(kev[i][0], kev[i][1])
-                q.qlora_linear_fwd(copies[i % ncopy], X, A, B, cfg.alpha, Y=Y, T=T, workspace=ws)
+                call(i)
             q.qlora_set_timing_events()
-            hip.record(e1, st)
-            ms = hip.elapsed_ms(e0, e1) / reps
             kms = sum(hip.elapsed_ms(a, b) for a, b in kev) / reps
+            # back to back: the same calls in one graph (side stream for capture)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                call(0)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    call(i)
+            g.replay()
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(3):
+                e0, e1 = hip.event(), hip.event()
+                hip.record(e0, st)
+                g.replay()
+                hip.record(e1, st)
+                ms = hip.elapsed_ms(e0, e1) / reps
+                best = ms if best is None else min(best, ms)
+            del g
             nbytes = decode_bytes(M, L.N, L.K, cfg.r)
-            gbs = nbytes / (kms * 1e-3) / 1e9
-            out.append({"W": f"{L.N}x{L.K}", "M": M, "kernel_us": round(kms * 1e3, 2),
+            gbs = nbytes / (best * 1e-3) / 1e9
+            out.append({"W": f"{L.N}x{L.K}", "M": M, "reps": reps, "graph_us": round(best * 1e3, 2),
                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                        "call_us": round(ms * 1e3, 2)})
+                        "kernel_us": round(kms * 1e3, 2), "bytes": nbytes})
         del copies, w0
         torch.cuda.empty_cache()
     return out
@@ -228,7 +262,9 @@ def bench_bf16_weight(hip, lay, reps=10):
     r=64): nf4_dequantize, the adapter merge and its inverse.  Algorithmic
     bytes: dequantize reads the NF4 weight (0.516 B/weight) and writes bf16
     (2 B/weight); merge also reads the adapters; unmerge reads and writes
-    bf16.  The 470 MB output alone exceeds the 256 MB Infinity Cache."""
+    bf16.  The NF4 input rotates over copies of >= 512 MB in total and the
+    two 470 MB bf16 buffers alternate, so the 256 MB Infinity Cache serves
+    neither side."""
     import torch
     import bit_nf4_quantized_17_amd as q
     st = torch.cuda.current_stream().cuda_stream
@@ -236,20 +272,28 @@ def bench_bf16_weight(hip, lay, reps=10):
     out2 = torch.empty_like(out)
     nk = lay.N * lay.K
     adapters = 2 * lay.r * (lay.N + lay.K)
+    # the NF4 input is taken in turn from copies that together exceed 512 MB
+    w0 = lay.w
+    wbytes = sum(t.numel() * t.element_size() for t in (w0.codes, w0.qscale, w0.dscale))
+    ncopy = max(2, -(-512 * 2**20 // wbytes))
+    ws = [w0] + [q.NF4Weight(w0.codes.clone(), w0.qscale.clone(), w0.dscale.clone(), w0.rows, w0.cols)
+                 for _ in range(ncopy - 1)]
+    outs = (out, out2)
     res = {}
     for name, fn, nbytes in (
-            ("dequantize", lambda: q.nf4_dequantize(lay.w, out=out), nk * (0.5 + 1 / 64 + 4 / 16384 + 2)),
-            ("merge", lambda: q.qlora_merge(lay.w, lay.A, lay.B, lay.alpha, out=out),
+            ("dequantize", lambda i: q.nf4_dequantize(ws[i % ncopy], out=outs[i % 2]),
+             nk * (0.5 + 1 / 64 + 4 / 16384 + 2)),
+            ("merge", lambda i: q.qlora_merge(ws[i % ncopy], lay.A, lay.B, lay.alpha, out=outs[i % 2]),
              nk * (0.5 + 1 / 64 + 4 / 16384 + 2) + adapters),
-            ("unmerge", lambda: q.qlora_unmerge(out, lay.A, lay.B, lay.alpha, out=out2),
+            ("unmerge", lambda i: q.qlora_unmerge(outs[i % 2], lay.A, lay.B, lay.alpha, out=outs[(i + 1) % 2]),
              nk * 4 + adapters)):
-        for _ in range(3):
-            fn()
+        for i in range(3):
+            fn(i)
         e0, e1 = hip.event(), hip.event()
         torch.cuda.synchronize()
         hip.record(e0, st)
-        for _ in range(reps):
-            fn()
+        for i in range(reps):
+            fn(i)
         hip.record(e1, st)
         ms = hip.elapsed_ms(e0, e1) / reps
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -257,7 +301,8 @@ def bench_bf16_weight(hip, lay, reps=10):
                      "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         if name != "dequantize":
             res[name]["r"] = lay.r
-    del out, out2
+        res[name]["input_copies"] = ncopy if name != "unmerge" else 2
+    del out, out2, ws
     torch.cuda.empty_cache()
     return res
 
@@ -307,7 +352,8 @@ def bench_dual(hip, lay, reps=10):
 def bench_formats(hip, lay, reps=10):
     """Codebook and scale-format variants on the up projection (28672x8192,
     4096 tokens, r=64): quantize and dequantize bandwidth and the fused
-    forward, for INT4 with E4M3 scales and for NF4 with fp32 block scales.
+    forward, for INT4 with E4M3 scales, NF4 with fp32 block scales and NF4
+    with uint8-linear double-quantized scales.
     Algorithmic bytes per weight: quantize 4 read + 0.5 + scale bytes written
     (1/64 + 4/16384 with double quantization, 4/64 without); dequantize the
     reverse plus 2 written."""
@@ -330,15 +376,15 @@ def bench_formats(hip, lay, reps=10):
         return hip.elapsed_ms(e0, e1) / reps
 
     res = []
-    for codebook, dq in (("int4", True), ("nf4", False)):
-        w = q.NF4Weight.empty(lay.N, lay.K, codebook=codebook, double_quant=dq)
+    for codebook, dq, fmt in (("int4", True, "e4m3"), ("nf4", False, "e4m3"), ("nf4", True, "uint8")):
+        w = q.NF4Weight.empty(lay.N, lay.K, codebook=codebook, double_quant=dq, dq_format=fmt)
         scale_b = (1 / 64 + 4 / 16384) if dq else 4 / 64
-        qms = timed(lambda: q.nf4_quantize(lay.W, out=w, codebook=codebook, double_quant=dq))
+        qms = timed(lambda: q.nf4_quantize(lay.W, out=w, codebook=codebook, double_quant=dq, dq_format=fmt))
         dms = timed(lambda: q.nf4_dequantize(w, out=out))
         fms = timed(lambda: q.qlora_linear_fwd(w, lay.X, lay.A, lay.B, lay.alpha, Y=lay.Y, T=lay.T,
                                                workspace=lay.wsf))
         qb, db = nk * (4 + 0.5 + scale_b), nk * (0.5 + scale_b + 2)
-        res.append({"format": f"{codebook}, {'E4M3 double-quantized' if dq else 'fp32'} scales",
+        res.append({"format": f"{codebook}, {(fmt.upper() + ' double-quantized') if dq else 'fp32'} scales",
                     "quantize_us": round(qms * 1e3, 1),
                     "quantize_frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "dequantize_us": round(dms * 1e3, 1),
@@ -427,6 +473,142 @@ def bench_library_reference(hip, layers, reps=10):
     return out
 
 
+def bench_training_configs(hip, reps=10):
+    """The three smaller training shapes, fwd + bwd of every linear (inputs
+    resident, weights quantized beforehand):
+      C1 tiny 256x256, 16 tokens, r=8 (latency-bound: us per fwd + bwd);
+      C2 7B attention projection 4096x4096, 4096 tokens, r=16;
+      C3 7B MLP gate/up 4096->11008 and down 11008->4096, 8192 tokens, r=64
+         (three forwards, then three backwards).
+    graph_us: the steps captured in one HIP graph and replayed back to back;
+    eager_us: host-launched steps (python + ctypes launch cost included)."""
+    import torch
+    import synthetic_inputs as si
+    st = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for tag, key, nrep in (("C1", "tiny_256", 200), ("C2", "attn_4096", reps), ("C3", "mlp7b_11008", reps)):
+        cfg = si.CONFIGS[key]
+        lays = [Layer(cfg, i) for i in range(len(cfg.layers))]
+        for lay in lays:
+            lay.quantize()
+
+        def step():
+            for lay in lays:
+                lay.fwd()
+            for lay in reversed(lays):
+                lay.bwd()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, st)
+        for _ in range(nrep):
+            step()
+        hip.record(e1, st)
+        eager_ms = hip.elapsed_ms(e0, e1) / nrep
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(nrep):
+                step()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_ms = None
+        for _ in range(3):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, st)
+            g.replay()
+            hip.record(e1, st)
+            ms = hip.elapsed_ms(e0, e1) / nrep
+            graph_ms = ms if graph_ms is None else min(graph_ms, ms)
+        del g
+        flops = sum(sum(lay.flops()[:2]) for lay in lays)
+        tf = flops / (graph_ms * 1e-3) / 1e12
+        res[tag] = {"workload": cfg.title, "flops_per_step": flops, "reps": nrep,
+                    "graph_us": round(graph_ms * 1e3, 2), "eager_us": round(eager_ms * 1e3, 2),
+                    "TFLOP/s": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del lays
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_context(hip):
+    """What the chip itself delivers, from the benchmark's probe kernels
+    (libqlora_probes.so, not part of the path) and torch's device copy:
+      mfma_loop: v_mfma_f32_32x32x16_bf16 on register operands, 8 waves a
+        compute unit, four accumulators a wave, zero and random operands;
+      hbm_read: 16-byte streaming loads over a 2 GiB buffer;
+      hbm_copy: torch copy_ of 1 GiB (read + write counted);
+      empty_kernel: back-to-back launches of an empty kernel in a HIP graph."""
+    import torch
+    import bit_nf4_quantized_17_amd as q
+    st = torch.cuda.current_stream().cuda_stream
+    P = ctypes.CDLL(os.path.join(ROOT, "bit_nf4_quantized_17_amd", "libqlora_probes.so"))
+    P.qlora_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    P.qlora_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    P.qlora_probe_empty.argtypes = [ctypes.c_void_p]
+    res = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, st)
+        for _ in range(reps):
+            fn()
+        hip.record(e1, st)
+        return hip.elapsed_ms(e0, e1) / reps
+
+    grid, iters = 512, 20000
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    flops = grid * 4 * iters * 4 * 32768
+    for zero in (1, 0):
+        ms = timed(lambda: P.qlora_probe_mfma(out.data_ptr(), iters, zero, grid, st), 3)
+        tf = flops / (ms * 1e-3) / 1e12
+        res["mfma_loop_" + ("zero" if zero else "random")] = {
+            "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: P.qlora_probe_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), 2048, st), 5)
+    gbs = buf.numel() / (ms * 1e-3) / 1e9
+    res["hbm_read"] = {"bytes": buf.numel(), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del buf
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    ms = timed(lambda: b.copy_(a), 5)
+    gbs = 2 * a.numel() / (ms * 1e-3) / 1e9
+    res["hbm_copy"] = {"bytes_each_way": a.numel(), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del a, b
+    n = 1000
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        P.qlora_probe_empty(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(n):
+            P.qlora_probe_empty(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, st)
+    g.replay()
+    hip.record(e1, st)
+    res["empty_kernel_us"] = round(hip.elapsed_ms(e0, e1) / n * 1e3, 3)
+    del g
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_quantize(hip, layers, reps=20):
     import torch
     st = torch.cuda.current_stream().cuda_stream
@@ -452,7 +634,7 @@ def bench_quantize(hip, layers, reps=20):
 def cpu_baseline(lay, target_s=15.0):
     import numpy as np
     import oracle
-    from tests.helpers import tensor_bits
+    from synthetic_inputs import tensor_bits
     threads = oracle.default_threads()
     codes = lay.w.codes.cpu().numpy()
     qs = lay.w.qscale.cpu().numpy()
@@ -612,6 +794,10 @@ def main():
         extras["adamw"] = bench_adamw(hip, layers)
         log("[bench] library reference")
         extras["context"] = {"hipblaslt_bf16_dense": bench_library_reference(hip, layers)}
+        log("[bench] chip context probes")
+        extras["context"].update(bench_context(hip))
+        log("[bench] training shapes C1-C3")
+        extras["training_configs"] = bench_training_configs(hip)
 
     cpu = None
     if not args.no_cpu_baseline:

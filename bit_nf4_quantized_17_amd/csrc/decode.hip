@@ -76,8 +76,7 @@ struct DecArgs {
   const uint8_t* codes; const uint8_t* qscale; const float* dscale;
   uint32_t N, K;
   float lv[16];                             // the codebook's levels
-  const float* tpart; int S;                // T partials [S][16][16 RT]
-  int u8;                                   // scale bytes are integers (uint8-linear), not E4M3
+  const float* tpart; int S, RT;            // T partials [S][16][16 RT]
   const u16* B; int r; float s;
   u16* Y; float* T_save;
 };
@@ -152,7 +151,7 @@ struct Chunk {
 };
 
 // Loads per chunk per wave, and D, the chunks loaded ahead: as deep as the
-// register ring allows (at most 180 of the 256 registers a wave of a
+// register ring allows (at most 160 of the 256 registers a wave of a
 // 512-lane workgroup may hold), at most 4, and within the 6-bit load
 // counter.
 template <int TR>
@@ -160,12 +159,12 @@ constexpr int lpc_of() { return TR + 4; }
 template <int TR>
 constexpr int depth_of() {
   constexpr int slot = 4 * TR + 16;          // registers of one ring slot
-  int d = 180 / slot - 1;                    // the ring takes at most 180
+  int d = 160 / slot - 1;                    // the ring takes at most 160
   d = d < 1 ? 1 : d > 4 ? 4 : d;
   return d * lpc_of<TR>() > 60 ? 60 / lpc_of<TR>() : d;
 }
 
-template <int TR, int RT>
+template <int TR, bool U8>
 __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   constexpr int D = depth_of<TR>();
   constexpr int NS = D + 1;
@@ -217,11 +216,11 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   float tpv[MAX_S];
   {
     const uint32_t m = (uint32_t)tid >> 5, j = (uint32_t)tid & 31u;
-    const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)RT);
+    const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)p.RT);
 #pragma unroll
     for (int sl = 0; sl < MAX_S; ++sl)
       tpv[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rT, sl < p.S && (int)j < p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)RT + j) : OOB, 0, 0));
+          rT, sl < p.S && (int)j < p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)p.RT + j) : OOB, 0, 0));
   }
 
   // issue iteration i's chunk into a ring slot.  Past the last iteration,
@@ -358,8 +357,8 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       const uint32_t kb_sw = 256u - ((qoff + 16u * (uint32_t)t * nbk) & 255u);
       const float2 dd = *reinterpret_cast<const float2*>(dtab + 2 * (16 * t + i16));
       const uint32_t q = *reinterpret_cast<const uint16_t*>(qtab + (uint32_t)(16 * t + i16) * nbk + kb);
-      const float v0 = p.u8 ? (float)(q & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 0);
-      const float v1 = p.u8 ? (float)((q >> 8) & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 1);
+      const float v0 = U8 ? (float)(q & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 0);
+      const float v1 = U8 ? (float)((q >> 8) & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 1);
       const float s0 = v0 * (kb < kb_sw ? dd.x : dd.y);
       const float s1 = v1 * (kb + 1u < kb_sw ? dd.x : dd.y);
 #pragma unroll
@@ -445,30 +444,26 @@ static uint32_t dyn_lds(const Plan& pl, int r, uint32_t K) {
   return std::max(sums, stream) + 32u * (uint32_t)pl.TR * (uint32_t)r;
 }
 
-template <int TR, int RT>
+template <int TR, bool U8>
 static hipError_t launch_one(const DecArgs& p, unsigned grid, uint32_t lds, hipStream_t st) {
-  const hipError_t attr = set_dynamic_lds(reinterpret_cast<const void*>(&k_decode<TR, RT>), MAX_DYN_LDS);
+  const hipError_t attr = set_dynamic_lds(reinterpret_cast<const void*>(&k_decode<TR, U8>), MAX_DYN_LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_decode<TR, RT>), dim3(grid), dim3(NTHREADS), lds, st, p);
+  hipLaunchKernelGGL((k_decode<TR, U8>), dim3(grid), dim3(NTHREADS), lds, st, p);
   return hipGetLastError();
 }
 
-template <int RT>
-static hipError_t launch_rt(const Plan& pl, const DecArgs& p, unsigned grid, uint32_t lds, hipStream_t st) {
+template <bool U8>
+static hipError_t launch_tr(const Plan& pl, const DecArgs& p, unsigned grid, uint32_t lds, hipStream_t st) {
   switch (pl.TR) {
-    case 1: return launch_one<1, RT>(p, grid, lds, st);
-    case 2: return launch_one<2, RT>(p, grid, lds, st);
-    case 3: return launch_one<3, RT>(p, grid, lds, st);
-    case 4: return launch_one<4, RT>(p, grid, lds, st);
-    case 5: return launch_one<5, RT>(p, grid, lds, st);
-    case 6: return launch_one<6, RT>(p, grid, lds, st);
-    case 7: return launch_one<7, RT>(p, grid, lds, st);
+    case 1: return launch_one<1, U8>(p, grid, lds, st);
+    case 2: return launch_one<2, U8>(p, grid, lds, st);
+    case 3: return launch_one<3, U8>(p, grid, lds, st);
+    case 4: return launch_one<4, U8>(p, grid, lds, st);
+    case 5: return launch_one<5, U8>(p, grid, lds, st);
+    case 6: return launch_one<6, U8>(p, grid, lds, st);
+    case 7: return launch_one<7, U8>(p, grid, lds, st);
     default: return hipErrorInvalidConfiguration;
   }
-}
-
-static hipError_t launch_plan(const Plan& pl, const DecArgs& p, unsigned grid, uint32_t lds, hipStream_t st) {
-  return pl.RT == 2 ? launch_rt<2>(pl, p, grid, lds, st) : launch_rt<1>(pl, p, grid, lds, st);
 }
 
 }  // namespace dec
@@ -505,12 +500,12 @@ hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A
   p.N = (uint32_t)w.N; p.K = (uint32_t)w.K;
   for (int i = 0; i < 16; ++i) p.lv[i] = w.lv[i];
   p.tpart = ws; p.S = S;
-  p.u8 = w.u8_scale ? 1 : 0;
+  p.RT = pl.RT;
   p.B = B; p.r = r; p.s = s;
   p.Y = Y; p.T_save = T_save;
   const unsigned grid = (unsigned)((w.N + 16 * pl.TR - 1) / (16 * pl.TR));
   const uint32_t lds = dec::dyn_lds(pl, r, (uint32_t)w.K);
-  return dec::launch_plan(pl, p, grid, lds, st);
+  return w.u8_scale ? dec::launch_tr<true>(pl, p, grid, lds, st) : dec::launch_tr<false>(pl, p, grid, lds, st);
 }
 
 }  // namespace qln

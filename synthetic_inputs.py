@@ -91,6 +91,19 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    """bf16 bit patterns (uint16) -> a torch bfloat16 tensor on `device` (a copy)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16).copy())
+    return t.view(torch.bfloat16).to(device)
+
+
+def tensor_bits(t) -> np.ndarray:
+    """A torch bf16 tensor's bit patterns as a host uint16 array."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
 def weight(cfg: Config, li: int) -> np.ndarray:
     """fp32 frozen weight [N, K] ~ N(0, w_std); with outlier_frac > 0 a Bernoulli
     mask of that rate multiplies entries by outlier_scale."""

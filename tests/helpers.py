@@ -21,15 +21,7 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def bf16_tensor(bits: np.ndarray, device="cuda"):
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16).copy())
-    return t.view(torch.bfloat16).to(device)
-
-
-def tensor_bits(t) -> np.ndarray:
-    import torch
-    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+from synthetic_inputs import bf16_tensor, tensor_bits  # noqa: E402,F401  (re-exported for the tests)
 
 
 def tensor_f64(t) -> np.ndarray:
