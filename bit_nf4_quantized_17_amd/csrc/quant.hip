@@ -266,6 +266,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   if (tid < 16) s_L[tid] = lv.v[tid];
   constexpr bool FP32 = FMT == SCALE_FP32;
   const float d = FP32 ? 0.0f : dscale[g];
+  const auto rQ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qscale), (short)0,
+                                                    FP32 ? 0 : (int)nblocks, 0x00020000);
   uint32_t c[DQ_STEPS], qv[DQ_STEPS];
   float sv[DQ_STEPS];
 #pragma unroll
@@ -275,12 +277,14 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
       c[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + (b0 + blk) * 32) +
                                         (lane & 7));
       if constexpr (FP32) sv[j] = dscale[b0 + blk];
-      else qv[j] = qscale[b0 + blk];
     } else {
       c[j] = 0;
-      qv[j] = 0;
       sv[j] = 0.0f;
     }
+    // the scale byte by a buffer load (past the blocks it reads 0), outside
+    // the branch: a conversion placed in the branch would wait for each load
+    if constexpr (!FP32)
+      qv[j] = __builtin_amdgcn_raw_buffer_load_b8(rQ, blk < nbw ? (uint32_t)(b0 + blk) : 0x80000000u, 0, 0);
   }
   __syncthreads();  // level table ready
 #pragma unroll
