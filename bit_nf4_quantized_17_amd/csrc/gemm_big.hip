@@ -51,7 +51,7 @@ namespace big {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int APITCH = BK + 8;          // A tile [256][72] bf16 (144-byte rows)
 constexpr int FPITCH = BK + 8;          // forward W tile [256 n][72]
-constexpr int TPITCH = BN + 16;         // backward W tile [64 n][272] (544-byte rows)
+constexpr int TPITCH = BN + 32;         // backward W tile [64 n][288] (576-byte rows)
 constexpr int A_ELEMS = BM * APITCH;    // 18432
 constexpr int BF_ELEMS = BN * FPITCH;   // 18432
 constexpr int BT_ELEMS = BK * TPITCH;   // 17408
