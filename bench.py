@@ -672,6 +672,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip decode/quantize bandwidth runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (for scaling HBM byte counters)")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="only run each decode shape three times (for profiler counter passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -690,6 +692,20 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": a.numel() * 4, "copies": 3}))
+        return
+    if args.profile_decode:
+        from synthetic_inputs import bf16_tensor
+        dc = si.CONFIGS["decode_8192_28672"]
+        for li, L in enumerate(dc.layers):
+            w = q.nf4_quantize(torch.from_numpy(si.weight(dc, li)).cuda())
+            A, B = (bf16_tensor(t) for t in si.adapters(dc, li))
+            for M in dc.decode_M:
+                X = bf16_tensor(si.activations(dc, li, M))
+                for _ in range(3):
+                    q.qlora_linear_fwd(w, X, A, B, dc.alpha)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_decode": [f"{L.N}x{L.K}" for L in dc.layers], "M": list(dc.decode_M),
+                          "calls_each": 3}))
         return
     hip = Hip()
     cfg = si.CONFIGS["mlp70b_28672"]

@@ -10,7 +10,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
+namespace qlprobe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -67,7 +67,9 @@ __global__ __launch_bounds__(256) void k_probe_read(const u32x4v* src, uint64_t 
 
 __global__ void k_probe_empty() {}
 
-}  // namespace
+}  // namespace qlprobe
+
+using namespace qlprobe;
 
 extern "C" {
 
