@@ -286,16 +286,33 @@ __device__ __forceinline__ u16* w_dst(u16* sB, int tid) {
   else return sB + (blk >> 2) * TPITCH + 64 * (blk & 3) + 32 * half;
 }
 
+// Backward tile swizzle: in row n, 16-byte chunk c (8 bf16) is stored at chunk
+// c ^ x with x = 2 * bit 4 of c ^ (n & 1), a permutation inside each aligned
+// group of four chunks.  A thread stores four consecutive chunks of a row and
+// eight threads fill a row, so without it the chunks 16 apart (256 bytes)
+// and those of the next row fell on the same LDS banks; with it the 16 lanes
+// of one store cycle use 16 distinct 4-bank groups, and the transposing reads
+// (4 rows x 4 aligned chunks a half-wave) still cover 64 distinct banks.
+__device__ __forceinline__ uint32_t t_swz(uint32_t chunk, uint32_t row) {
+  return ((chunk >> 3) & 2u) ^ (row & 1u);
+}
+// the XOR of the thread's own chunks (all four share it)
+template <int MODE>
+__device__ __forceinline__ uint32_t w_swz(int tid) {
+  if constexpr (MODE == MODE_FWD) return 0u;
+  else return t_swz(4u * (uint32_t)(tid & 7), (uint32_t)(tid >> 3));
+}
+
 // dequantize the thread's half block and store its 32 bf16 values at dst
 __device__ __forceinline__ void store_w(const StageW& st, const float (&mv)[8], uint32_t flip,
-                                        uint32_t qor, u16* dst) {
+                                        uint32_t qor, u16* dst, uint32_t swz) {
   const Table t = make_table(mv, stage_scale(st, qor));
   const uint32_t c[4] = {st.c.x, st.c.y, st.c.z, st.c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t o[4];
     dequant8(t, c[i], flip, o);
-    *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + 8 * ((uint32_t)i ^ swz)) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -325,7 +342,7 @@ __device__ __forceinline__ void lora_b_tile(const BigArgs& p, u16* sB, int64_t j
       for (int e = 0; e < 8; ++e)
         if (c + e < cols) v[e >> 1] |= (uint32_t)p.lb[row * ld + c + e] << (16 * (e & 1));
     }
-    *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<uint4*>(dst + 8 * ((uint32_t)q ^ w_swz<MODE>(tid))) = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -371,11 +388,13 @@ __device__ __forceinline__ bf16x8_t read_b(const u16* sB, int wn, int b, int ks,
     const int L = lane & 15;
     const int col = wn * 64 + b * 32 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
     const int row = ks * 16 + 8 * (lane >> 5) + (L >> 2);
+    // rows row and row + 4 have the same parity, so the same swizzle
+    const int scol = col ^ (8 * (int)t_swz((uint32_t)col >> 3, (uint32_t)row));
     const lds_short* base = (const lds_short*)(sB);
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + row * TPITCH + col));
+        (lds_s16x4*)(base + row * TPITCH + scol));
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + (row + 4) * TPITCH + col));
+        (lds_s16x4*)(base + (row + 4) * TPITCH + scol));
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
     s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
@@ -429,7 +448,7 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
                                                StageA& ra, StageW& w,
                                                u16* sA_next, u16* wdst_next, int tid,
                                                const NextLoads& nl, const float (&mv)[8],
-                                               uint32_t flip) {
+                                               uint32_t flip, uint32_t wswz) {
   bf16x8_t fa[2][4], fb[2][2];
   frags<MODE>(fa[0], fb[0], sA, sB, wm, wn, 0, lane);
   const Table t = make_table(mv, stage_scale(w, nl.bf->qor));
@@ -455,7 +474,7 @@ __device__ __forceinline__ void step_pipelined(f32x16_t (&acc)[4][2], const u16*
     {
       uint32_t o[4];
       dequant8(t, c[ks], flip, o);
-      *reinterpret_cast<uint4*>(wdst_next + 8 * ks) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(wdst_next + 8 * ((uint32_t)ks ^ wswz)) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(sA_next + (tid / 8 + 64 * ks) * APITCH + (tid % 8) * 8) = ra.v[ks];
       ra.v[ks] = bload16(nl.bf->a, nl.a_base + ks * nl.a_step + 2 * nl.a_c0);
     }
@@ -563,7 +582,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
   load_a(ra, bf, a_base, a_step, 0);
   load_w(w0, bf, w_n(0), w_k(0), whalf, K, true);
   store_a(ra, sA[0], tid);
-  store_w(w0, mv, flip, bf.qor, wdst0);
+  const uint32_t wswz = w_swz<MODE>(tid);
+  store_w(w0, mv, flip, bf.qor, wdst0, wswz);
   load_a(ra, bf, a_base, a_step, BK);
   load_w(w1, bf, w_n(1), w_k(1), whalf, K, 1 < nk);
   load_w(w0, bf, w_n(2), w_k(2), whalf, K, 2 < nk);
@@ -576,14 +596,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_big(BigArgs p) {
     {
       const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 2) * BK), w_n(kt + 3), w_k(kt + 3), whalf, K,
                          kt + 3 < nk};
-      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl, mv, flip);
+      step_pipelined<MODE>(acc, sA[0], sB[0], wm, wn, lane, ra, w1, sA[1], wdst1, tid, nl, mv, flip, wswz);
     }
     __syncthreads();
     // buffer 1 holds stage kt+1; ra = A(kt+2), w0 = W(kt+2), w1 = W(kt+3)
     {
       const NextLoads nl{&bf, a_base, a_step, (uint32_t)((kt + 3) * BK), w_n(kt + 4), w_k(kt + 4), whalf, K,
                          kt + 4 < nk};
-      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl, mv, flip);
+      step_pipelined<MODE>(acc, sA[1], sB[1], wm, wn, lane, ra, w0, sA[0], wdst0, tid, nl, mv, flip, wswz);
     }
     __syncthreads();
   }
