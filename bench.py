@@ -542,8 +542,12 @@ def bench_context(hip):
     (libqlora_probes.so, not part of the path) and torch's device copy:
       mfma_loop: v_mfma_f32_32x32x16_bf16 on register operands, 8 waves a
         compute unit, four accumulators a wave, zero and random operands;
+      mfma_lds: the same MFMAs fed from LDS at the fused GEMMs' 128 x 64
+        wave tile (six 16-byte fragment reads per eight MFMAs), random operands;
       hbm_read: 16-byte streaming loads over a 2 GiB buffer;
       hbm_copy: torch copy_ of 1 GiB (read + write counted);
+      lds_read: 16-byte conflict-free LDS reads, one 512-thread workgroup a
+        compute unit; bytes per clock per compute unit from the shader clock;
       empty_kernel: back-to-back launches of an empty kernel in a HIP graph."""
     import torch
     import bit_nf4_quantized_17_amd as q
@@ -552,6 +556,10 @@ def bench_context(hip):
     P.qlora_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     P.qlora_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                    ctypes.c_void_p]
+    P.qlora_probe_mfma_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    P.qlora_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
     P.qlora_probe_empty.argtypes = [ctypes.c_void_p]
     res = {}
 
@@ -573,6 +581,13 @@ def bench_context(hip):
         tf = flops / (ms * 1e-3) / 1e12
         res["mfma_loop_" + ("zero" if zero else "random")] = {
             "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    grid, iters = 256, 4000
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    flops = grid * 8 * iters * 32 * 32768
+    ms = timed(lambda: P.qlora_probe_mfma_lds(out.data_ptr(), iters, 0, grid, st), 3)
+    tf = flops / (ms * 1e-3) / 1e12
+    res["mfma_lds_random"] = {"TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del out
     buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
     sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
     ms = timed(lambda: P.qlora_probe_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), 2048, st), 5)
@@ -585,6 +600,16 @@ def bench_context(hip):
     gbs = 2 * a.numel() / (ms * 1e-3) / 1e9
     res["hbm_copy"] = {"bytes_each_way": a.numel(), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
     del a, b
+    grid, iters = 256, 20000
+    lsink = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    cyc = torch.zeros(grid, dtype=torch.int64, device="cuda")
+    ms = timed(lambda: P.qlora_probe_lds(lsink.data_ptr(), cyc.data_ptr(), iters, grid, st), 3)
+    per_wg = 512 * iters * 8 * 16
+    cycles = cyc.double().median().item()
+    res["lds_read"] = {"TB/s": round(grid * per_wg / (ms * 1e-3) / 1e12, 2),
+                       "bytes_per_clk_cu": round(per_wg / cycles, 1),
+                       "clock_GHz": round(cycles / (ms * 1e-3) / 1e9, 3)}
+    del lsink, cyc
     n = 1000
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
