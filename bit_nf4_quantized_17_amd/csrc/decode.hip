@@ -3,51 +3,52 @@
 // bfloat16 for the matrix product and adds the LoRA path.
 //
 // At M <= 16 the layer is bound by streaming the packed weight (0.516 bytes
-// per weight) from HBM, which leaves about three vector-ALU operations per
-// weight at full bandwidth -- less than an exact per-element dequantization
-// costs.  So this path factors the block scale out of the product:
-//   Y[m][n] = sum_blocks s_b * ( sum_{k in block} X[m][k] * bf16(L[code]) )
-//           + s_lora * sum_j T[m][j] B[n][j],      T = X A^T (fp32)
-// bf16(L[code]) comes from an LDS table indexed by one code byte (two codes
-// -> one bf16 pair), with one copy per lane so that lookups never share a
-// bank; each 64-code block is one pair of v_mfma_f32_16x16x32_bf16 into a
-// fresh accumulator, which is then scaled by the block's restored scale
-// s_b = fl32(v(q) * d) (v: the E4M3 value of the scale byte, or the byte
-// as an integer for uint8-linear scales) and added in fp32.  (The prefill and training
-// kernels multiply the exactly dequantized bf16 weight instead; both round
-// the weight's relative value once to bf16 precision.)
+// per weight) from HBM.  This path multiplies the same bf16 weight as the
+// prefill kernels, w' = bf16(fl32(L[code] * s_b)) with s_b = fl32(v(q_b) d_g),
+// dequantized in registers (about four vector-ALU operations per weight), and
+// adds the LoRA term as their prologue does:
+//   Y = X W'^T + bf16(s_lora T) B^T,      T = X A^T (fp32)
+// (Taking the block scale out of the product -- bf16(L[code]) from a table,
+// s_b applied to each block's partial sum -- costs less than one operation
+// per weight, but it rounds the unscaled level instead of the weight: on
+// weights with outliers that moves outputs past the elementwise tolerance
+// already at K = 8192.)
 //
 // Two launches.  The first sums T = X A^T over S slices of the contraction
 // (S x RT small workgroups, fp32 partials in the workspace).  The second
 // streams the weight with no communication between workgroups: a workgroup
 // owns 16 * TR consecutive output columns (W rows, TR <= 7) over the whole
-// contraction, so it finishes its outputs itself; it adds up the S partials
-// of T in a fixed order for its LoRA term.  Its grid is about one workgroup
-// per compute unit.  The 8-bit block scales of its rows are one contiguous
-// run of bytes, which it copies to LDS at the start.
+// contraction, so it finishes its outputs itself; at the end it adds up the
+// S partials of T in a fixed order for its LoRA term.  Its grid is about one
+// workgroup per compute unit.  The 8-bit block scales of its rows are one
+// contiguous run of bytes; at the start it restores them into an fp32 table
+// in LDS, so a row's blocks may span any number of scale groups.
 //
 // The eight waves split the contraction into chunks of 128 (two blocks, 64
 // code bytes of a row), wave w taking every eighth chunk from chunk w, and
 // run independently until the final sums: no LDS staging and no barrier in
-// the stream.  Per chunk and
-// 16-row tile a wave loads the codes straight into registers -- lane
-// (n = lane % 16, g = lane / 16) takes bytes [16 g, 16 g + 16) of row n --
-// and one v_permlane32_swap per register pair moves them so that registers
-// x, y of every lane hold block 0 of the chunk and z, w block 1 (the swap
-// exchanges the upper lanes of one register with the lower lanes of the
-// other).  Each register then feeds one MFMA whose 32 contraction slots all
-// lie in one block; the X fragments are loaded in the same contraction
-// order (lane group g, register v: chunk offset 64 [v in z, w] + 8 [v in y,
-// w] + 32 (g & 1) + 16 (g >> 1)).  Loads run D chunks ahead in a register
-// ring.  Since the waves run at the same pace, the two halves of each
-// 128-byte line reach L2 close together and the line is fetched from HBM
-// once (measured: a wave that read both halves itself, one chunk apart,
-// fetched 1.7 times the weight's bytes).  The workgroups start at different
-// groups of chunks (if every workgroup read the same column window of its
-// rows at the same time, the requests would pile onto a few memory
-// channels).  The
-// eight waves' sums are added in LDS in wave order, so results do not depend
-// on timing.
+// the stream.  Per chunk and 16-row tile a wave loads the codes straight
+// into registers -- lane (n = lane % 16, g = lane / 16) takes bytes
+// [16 g, 16 g + 16) of row n, codes 32 g .. 32 g + 31 of the chunk, all in
+// block g / 2 of it -- and register v (8 codes) of every lane becomes the
+// weight operand of MFMA v, whose 32 contraction slots are codes 32 g + 8 v
+// .. + 7 of the four lane groups.  A lane's 16 scaled levels are built by
+// the two lanes of its row and block (lanes 16 apart: one scales levels
+// 0 .. 7, the other 8 .. 15, and a v_permlane16_swap of each plane word with
+// itself hands both lanes both halves) as low-byte and high-byte planes, and
+// each code is looked up with byte permutes.  The even and the odd codes of
+// a register are looked up separately, so an operand holds its elements in
+// the order 0, 2, 4, 6, 1, 3, 5, 7; the X fragments (row m, the same 8
+// contraction indices) are permuted the same way.  Loads run D chunks
+// ahead in a register ring.  Since the waves run at the same pace, the two
+// halves of each 128-byte line reach L2 close together and the line is
+// fetched from HBM once (measured: a wave that read both halves itself, one
+// chunk apart, fetched 1.7 times the weight's bytes).  The workgroups start
+// at different groups of chunks (if every workgroup read the same column
+// window of its rows at the same time, the requests would pile onto a few
+// memory channels).  The eight waves' sums are added in LDS in wave order
+// (wave t first adds the LoRA term of tile t to its own), so results do not
+// depend on timing.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -61,13 +62,23 @@ namespace dec {
 
 constexpr int WAVES = 8;
 constexpr int NTHREADS = 64 * WAVES;
-constexpr int LUT_WORDS = 256 * 64;     // 256 byte values x 64 lanes, 64 KB (static LDS)
 constexpr int CHUNK = 128;              // contraction elements per chunk (two blocks)
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every range this path uses
-constexpr int MAX_R = 32;               // ranks the fused T handles (two 16-rank tiles)
+constexpr int MAX_R = QLN_MAX_RANK;     // ranks (T is kept [16][MAX_R] in LDS)
 constexpr int MAX_TR = 7;               // 16-row tiles per workgroup
-constexpr int MAX_DYN_LDS = 94 * 1024;  // dynamic LDS limit set on the kernels (they use <= 65 KB)
+constexpr int MAX_DYN_LDS = 160 * 1024; // dynamic LDS limit set on the kernels (all of it)
+constexpr uint32_t MAX_K = 65536;       // longest contraction
 constexpr int MAX_S = 16;               // slices of the T partials
+constexpr int QPASS = 4;                // 16-byte scale loads a thread
+constexpr uint32_t QBYTES = 16u * NTHREADS * QPASS;   // scale bytes a workgroup can restore (32 KB)
+constexpr int BCH = (16 * MAX_TR * (MAX_R + 8) / 8 + NTHREADS - 1) / NTHREADS;   // 16-byte B chunks a thread
+
+// floats at the start of the dynamic LDS: the per-wave sums [8][TR][256]
+// after the stream, the restored block scales [16 TR][K / 64] during it
+__host__ __device__ inline uint32_t region0_floats(int TR, uint32_t K) {
+  const uint32_t sums = (uint32_t)WAVES * 256u, scales = 16u * (K / 64u);
+  return (sums > scales ? sums : scales) * (uint32_t)TR;
+}
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
@@ -142,12 +153,70 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// A block's 16 bf16 weights bf16(fl32(L[c] * s)) as a low-byte and a
+// high-byte plane (word j holds levels 4j .. 4j + 3).  lv8: this lane's
+// levels, 0 .. 7 in even 16-lane rows and 8 .. 15 in odd ones; the two lanes
+// 16 apart share a row and a block, and v_permlane16_swap of a word with
+// itself returns the even row's word and the odd row's word in both lanes.
+struct Table {
+  uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ Table make_table(const float (&lv8)[8], float s) {
+  uint32_t pk[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(lv8[2 * j] * s, lv8[2 * j + 1] * s);
+  Table t;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t lo = __builtin_amdgcn_perm(pk[2 * q + 1], pk[2 * q], 0x06040200u);
+    const uint32_t hi = __builtin_amdgcn_perm(pk[2 * q + 1], pk[2 * q], 0x07050301u);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    t.lo[q] = l[0]; t.lo[2 + q] = l[1];
+    t.hi[q] = h[0]; t.hi[2 + q] = h[1];
+  }
+  return t;
+}
+
+// four 4-bit indices (one per byte) -> their bf16 low bytes and high bytes.
+// Byte selectors past 12 read as 0xFF, so each half of the table is looked
+// up with the other half's indices pushed past 16 and the two are AND-ed.
+__device__ __forceinline__ void lookup4(const Table& t, uint32_t idx, uint32_t& lo, uint32_t& hi) {
+  const uint32_t selA = __builtin_amdgcn_bitop3_b32(idx, idx << 1, 0x10101010u, 0xF8);  // 8..15 -> 24..31 (0xFF)
+  const uint32_t selB = selA ^ 0x18181818u;                // indices 0..7 -> 24..31, 8..15 -> 0..7
+  lo = __builtin_amdgcn_perm(t.lo[1], t.lo[0], selA) & __builtin_amdgcn_perm(t.lo[3], t.lo[2], selB);
+  hi = __builtin_amdgcn_perm(t.hi[1], t.hi[0], selA) & __builtin_amdgcn_perm(t.hi[3], t.hi[2], selB);
+}
+
+// 8 codes (element e in bits 4e .. 4e + 3) -> an MFMA operand of their bf16
+// weights in the element order 0, 2, 4, 6, 1, 3, 5, 7
+__device__ __forceinline__ bf16x8_t dequant8(const Table& t, uint32_t c) {
+  uint32_t l, h;
+  u32x4v o;
+  lookup4(t, c & 0x0F0F0F0Fu, l, h);
+  o[0] = __builtin_amdgcn_perm(h, l, 0x05010400u);
+  o[1] = __builtin_amdgcn_perm(h, l, 0x07030602u);
+  lookup4(t, (c >> 4) & 0x0F0F0F0Fu, l, h);
+  o[2] = __builtin_amdgcn_perm(h, l, 0x05010400u);
+  o[3] = __builtin_amdgcn_perm(h, l, 0x07030602u);
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+// 8 bf16 in element order -> the order 0, 2, 4, 6, 1, 3, 5, 7
+__device__ __forceinline__ bf16x8_t evens_then_odds(bf16x8_t x) {
+  const u32x4v w = __builtin_bit_cast(u32x4v, x);
+  const u32x4v o = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
+                    __builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
 // One wave's register loads of one chunk: per tile the codes of the lane's
 // row, and the X fragments of the chunk's four MFMAs (shared by every tile).
 template <int TR>
 struct Chunk {
   u32x4v c[TR];           // row n0 + 16 t + lane % 16, code bytes [16 g, 16 g + 16) of the chunk
-  bf16x8_t x[4];          // X[m = lane % 16][chunk offset of register v .. + 8], v = x, y, z, w
+  bf16x8_t x[4];          // X[m = lane % 16][chunk offset 32 g + 8 v .. + 8], v = 0 .. 3
 };
 
 // Loads per chunk per wave, and D, the chunks loaded ahead: as deep as the
@@ -169,7 +238,6 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   constexpr int D = depth_of<TR>();
   constexpr int NS = D + 1;
   constexpr int LPC = lpc_of<TR>();
-  __shared__ __attribute__((aligned(16))) uint32_t lut[LUT_WORDS];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -194,33 +262,23 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   // this lane's code offset at chunk 0 of tile 0 (tile t adds 16 t rows;
   // rows past N fall past the buffer's range and read zeros)
   const uint32_t coff = (n0 + (uint32_t)i16) * RB + 16u * (uint32_t)g;
-  const uint32_t qoff = (n0 + (uint32_t)i16) * nbk;   // the row's first scale byte
-  // contraction offset of lane group g within a chunk's register x
-  const uint32_t kg = 32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1);
-  const uint32_t xoff = i16 < p.M ? (uint32_t)i16 * K * 2u + 2u * kg : OOB;
+  // X row m = lane % 16 at contraction offset 32 g of a chunk (rows past M read zero)
+  const uint32_t xoff = i16 < p.M ? (uint32_t)i16 * K * 2u + 64u * (uint32_t)g : OOB;
 
   // ---- the workgroup's block scales, 16 TR nbk contiguous bytes from
-  //      n0 nbk (at most 28 KB), 16 bytes a thread and pass; rows past N
-  //      read zeros ----
-  constexpr int QPASS = (16 * MAX_TR * 256 + 16 * NTHREADS - 1) / (16 * NTHREADS);
+  //      n0 nbk (at most QBYTES), 16 bytes a thread and pass, with the group
+  //      constant of each thread's 16 (n0 nbk is a multiple of 16, so they
+  //      lie in one group of 256); rows past N read zeros ----
   const uint32_t qbytes = 16u * (uint32_t)TR * nbk;
+  const auto rD = rsrc(p.dscale, 4u * ((N * nbk + 255u) / 256u));
   u32x4v qv[QPASS];
+  float qd[QPASS];
 #pragma unroll
   for (int i = 0; i < QPASS; ++i) {
     const uint32_t o = 16u * (uint32_t)(tid + NTHREADS * i);
     qv[i] = __builtin_amdgcn_raw_buffer_load_b128(rQ, o < qbytes ? n0 * nbk + o : OOB, 0, 0);
-  }
-
-  // ---- the sum of the T partials for thread (m, j) = (tid / 32, tid % 32),
-  //      in slice order ----
-  float tpv[MAX_S];
-  {
-    const uint32_t m = (uint32_t)tid >> 5, j = (uint32_t)tid & 31u;
-    const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)p.RT);
-#pragma unroll
-    for (int sl = 0; sl < MAX_S; ++sl)
-      tpv[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rT, sl < p.S && (int)j < p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)p.RT + j) : OOB, 0, 0));
+    qd[i] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rD, o < qbytes ? 4u * ((n0 * nbk + o) >> 8) : OOB, 0, 0));
   }
 
   // issue iteration i's chunk into a ring slot.  Past the last iteration,
@@ -238,50 +296,45 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       f.c[t] = __builtin_amdgcn_raw_buffer_load_b128(rC, co + 16u * (uint32_t)t * RB, 0, 0);
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      f.x[v] = ld16(rX, xoff + 256u * c + 128u * (uint32_t)(v >> 1) + 16u * (uint32_t)(v & 1));
+      f.x[v] = ld16(rX, xoff + 256u * c + 16u * (uint32_t)v);
   };
 
-  // ---- the lookup table, from the kernel arguments: word e holds the pair
-  //      (byte & 15, byte >> 4) of byte e / 64; thread tid writes bytes
-  //      wave + 8i (the wave's low level is picked with uniform selects) ----
-  {
-    float lo0 = p.lv[0], lo1 = p.lv[8];
+  // ---- this lane's eight levels, 0 .. 7 in even 16-lane rows and 8 .. 15
+  //      in odd ones ----
+  float lv8[8];
 #pragma unroll
-    for (int k = 1; k < 8; ++k)
-      if (wave == k) { lo0 = p.lv[k]; lo1 = p.lv[k + 8]; }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) lut[tid + NTHREADS * i] = pack_bf16x2((i & 1) ? lo1 : lo0, p.lv[i >> 1]);
-  }
+  for (int e = 0; e < 8; ++e) lv8[e] = (g & 1) ? p.lv[8 + e] : p.lv[e];
 
-  // ---- the LoRA factor B of this workgroup's rows: 16 TR rows x r bf16 =
-  //      2 TR r 16-byte chunks at byte 32 TR r blockIdx, one per thread,
-  //      held in registers until the epilogue (element by element: the
-  //      chunk that holds the end of B may hold bytes past it, which read
-  //      as zero) ----
+  // ---- the LoRA factor B of this workgroup's rows, zero-padded to
+  //      [16 TR][BP] bf16 (BP = RP + 8, RP = r rounded up to 32): 16-byte
+  //      chunk q is row q / (BP / 8), ranks 8 (q % (BP / 8)) .. + 8, up to
+  //      BCH chunks a thread (a whole chunk in one load when r % 8 == 0,
+  //      else element by element; ranks past r and rows past N read zero) ----
+  const uint32_t RP = ((uint32_t)p.r + 31u) & ~31u, BP = RP + 8u, BQ = BP / 8u;
   const uint32_t bsize = N * (uint32_t)p.r * 2u;
   const auto rB = rsrc(p.B, bsize);
-  const uint32_t bchunks = 2u * (uint32_t)TR * (uint32_t)p.r;
-  const uint32_t boff = 32u * (uint32_t)TR * (uint32_t)p.r * (uint32_t)blockIdx.x + 16u * (uint32_t)tid;
-  u32x4v bchunk;
+  const uint32_t bchunks = 16u * (uint32_t)TR * BQ;
+  const bool bvec = (p.r & 7) == 0;
+  u32x4v bch[BCH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t o = boff + 4u * (uint32_t)i;
-    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)tid < bchunks && o < bsize ? o : OOB, 0, 0);
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)tid < bchunks && o + 2u < bsize ? o + 2u : OOB, 0, 0);
-    bchunk[i] = lo | (hi << 16);
-  }
-
-  // ---- the group constants of the workgroup's rows: row c's blocks lie in
-  //      at most two groups of 256 (K <= 16384), g0 = (n nbk) >> 8 and
-  //      g0 + 1; thread c < 16 TR loads both now and writes them to LDS
-  //      after the prologue ----
-  const auto rD = rsrc(p.dscale, 4u * ((N * nbk + 255u) / 256u));
-  float dl0 = 0.0f, dl1 = 0.0f;
-  if (tid < 16 * TR) {
-    const uint32_t n = n0 + (uint32_t)tid;
-    const uint32_t g0 = (n * nbk) >> 8;
-    dl0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, n < N ? 4u * g0 : OOB, 0, 0));
-    dl1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, n < N ? 4u * (g0 + 1u) : OOB, 0, 0));
+  for (int i = 0; i < BCH; ++i) {
+    const uint32_t q = (uint32_t)(tid + NTHREADS * i);
+    const uint32_t c = q / BQ, j0 = 8u * (q - c * BQ);
+    const uint32_t row0 = ((n0 + c) * (uint32_t)p.r + j0) * 2u;   // byte offset of (row, j0)
+    const bool live = q < bchunks && n0 + c < N && j0 < (uint32_t)p.r;
+    if (bvec) {
+      bch[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, live ? row0 : OOB, 0, 0);
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t j = j0 + 2u * (uint32_t)w;
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+            rB, live && j < (uint32_t)p.r ? row0 + 4u * (uint32_t)w : OOB, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+            rB, live && j + 1u < (uint32_t)p.r ? row0 + 4u * (uint32_t)w + 2u : OOB, 0, 0);
+        bch[i][w] = lo | (hi << 16);
+      }
+    }
   }
 
   // ---- prologue: the first D chunks, each group of loads kept whole and
@@ -294,45 +347,41 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // T, the scales, the rows of B and the group constants go to LDS now
-  // (their loads are older than the prologue's); scales and constants share
-  // the space of the per-wave sums, which are written only after every wave
-  // has left the stream
+  // The restored scales and the rows of B go to LDS now (their loads are
+  // older than the prologue's); the scales share the space of the per-wave
+  // sums, which are written only after every wave has left the stream
   float* red = reinterpret_cast<float*>(smem);                 // [8 waves][TR][16 m][16 n]
-  float* ttab = red + WAVES * TR * 256;                        // [16 m][MAX_R]
-  u16* btab = reinterpret_cast<u16*>(ttab + 16 * MAX_R);       // B rows of the workgroup [16 TR][r]
-  float* dtab = red;                                           // [16 TR rows][2]
-  uint8_t* qtab = smem + 16 * 16 * MAX_TR;                     // [16 TR rows][nbk] scale bytes
+  float* stab = red;                                           // [16 TR rows][nbk] block scales
+  float* ttab = red + region0_floats(TR, K);                   // [16 m][MAX_R]
+  u16* btab = reinterpret_cast<u16*>(ttab + 16 * MAX_R);       // B rows of the workgroup [16 TR][BP]
   wait_vm<LPC * D>();
-  {
-    // T[m][j] for thread (m, j) = (tid / 32, tid % 32): slices past S hold zero
-    float tval = 0.0f;
 #pragma unroll
-    for (int sl = 0; sl < MAX_S; ++sl) tval += tpv[sl];
-    const int m = tid >> 5, j = tid & 31;
-    ttab[m * MAX_R + j] = tval;
-    if (blockIdx.x == 0 && m < p.M && j < p.r) p.T_save[m * p.r + j] = tval;
+  for (int i = 0; i < BCH; ++i) {
+    const uint32_t q = (uint32_t)(tid + NTHREADS * i);
+    if (q < bchunks) *reinterpret_cast<u32x4v*>(btab + 8u * q) = bch[i];
   }
-  if ((uint32_t)tid < bchunks) *reinterpret_cast<u32x4v*>(reinterpret_cast<uint8_t*>(btab) + 16u * (uint32_t)tid) = bchunk;
-  if (tid < 16 * TR) { dtab[2 * tid] = dl0; dtab[2 * tid + 1] = dl1; }
+  // s_b = fl32(v(q_b) * d_g): v the E4M3 value of the byte, or the byte as an
+  // integer for uint8-linear scales
 #pragma unroll
   for (int i = 0; i < QPASS; ++i) {
     const uint32_t o = 16u * (uint32_t)(tid + NTHREADS * i);
-    if (o < qbytes) *reinterpret_cast<u32x4v*>(qtab + o) = qv[i];
+    if (o < qbytes) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t q = qv[i][w];
+        u32x4v sv;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t qb = q >> (8 * b);
+          const float v = U8 ? (float)(qb & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)qb, 0);
+          sv[b] = __float_as_uint(v * qd[i]);
+        }
+        *reinterpret_cast<u32x4v*>(stab + o + 4u * (uint32_t)w) = sv;
+      }
+    }
   }
 
-  __syncthreads();   // the lookup table is complete
-
-  const uint32_t lane4 = (uint32_t)lane * 4u;
-  // LDS address of (byte e of word c, this lane's copy) = byte << 8 | lane * 4
-  auto lookup = [&](uint32_t c, int e) -> uint32_t {
-    const uint32_t addr = __builtin_amdgcn_perm(c, lane4, 0x0C0C0400u + ((uint32_t)e << 8));
-    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lut) + addr);
-  };
-  auto operand = [&](uint32_t c) -> bf16x8_t {
-    const u32x4v w = {lookup(c, 0), lookup(c, 1), lookup(c, 2), lookup(c, 3)};
-    return __builtin_bit_cast(bf16x8_t, w);
-  };
+  __syncthreads();   // the restored scales are complete
 
   f32x4_t acc[TR];
 #pragma unroll
@@ -342,27 +391,18 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     if (i >= G) return;
     const int c = chunk_of(i);
     if (c >= C) return;
-    const uint32_t kb = 2u * (uint32_t)c;   // first block of the chunk within the row
+    // the lane's block within the row: two per chunk, lane groups 0, 1 in the first
+    const uint32_t kb = 2u * (uint32_t)c + ((uint32_t)g >> 1);
+    bf16x8_t xp[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xp[v] = evens_then_odds(f.x[v]);
 #pragma unroll
     for (int t = 0; t < TR; ++t) {
-      // registers x, y <- block kb, z, w <- block kb + 1 (see the header)
-      const auto sxz = __builtin_amdgcn_permlane32_swap(f.c[t].x, f.c[t].z, false, false);
-      const auto syw = __builtin_amdgcn_permlane32_swap(f.c[t].y, f.c[t].w, false, false);
-      f32x4_t t0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[0], operand(sxz[0]), t0, 0, 0, 0);
-      t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[1], operand(syw[0]), t0, 0, 0, 0);
-      t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[2], operand(sxz[1]), t1, 0, 0, 0);
-      t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[3], operand(syw[1]), t1, 0, 0, 0);
-      // the row's first block in its second group
-      const uint32_t kb_sw = 256u - ((qoff + 16u * (uint32_t)t * nbk) & 255u);
-      const float2 dd = *reinterpret_cast<const float2*>(dtab + 2 * (16 * t + i16));
-      const uint32_t q = *reinterpret_cast<const uint16_t*>(qtab + (uint32_t)(16 * t + i16) * nbk + kb);
-      const float v0 = U8 ? (float)(q & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 0);
-      const float v1 = U8 ? (float)((q >> 8) & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)q, 1);
-      const float s0 = v0 * (kb < kb_sw ? dd.x : dd.y);
-      const float s1 = v1 * (kb + 1u < kb_sw ? dd.x : dd.y);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] += s0 * t0[e] + s1 * t1[e];
+      const Table tb = make_table(lv8, stab[(uint32_t)(16 * t + i16) * nbk + kb]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[0], dequant8(tb, f.c[t].x), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[1], dequant8(tb, f.c[t].y), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[2], dequant8(tb, f.c[t].z), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[3], dequant8(tb, f.c[t].w), acc[t], 0, 0, 0);
     }
   };
 
@@ -384,8 +424,54 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   }
   wait_vm<0>();
 
-  // ---- sums over the waves (fixed order), LoRA term, store ----
-  __syncthreads();   // every wave is done
+  // ---- T = the sum of the partials in slice order, [16 m][MAX_R] (ranks
+  //      past r and rows past M hold zero); workgroup 0 also stores it ----
+  {
+    const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)p.RT);
+    constexpr int TP = 16 * MAX_R / NTHREADS;
+    float tp[TP][MAX_S];
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      const uint32_t pr = (uint32_t)(tid + NTHREADS * i), m = pr / MAX_R, j = pr % MAX_R;
+#pragma unroll
+      for (int sl = 0; sl < MAX_S; ++sl)
+        tp[i][sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rT, sl < p.S && j < (uint32_t)p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)p.RT + j) : OOB,
+            0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      const int pr = tid + NTHREADS * i, m = pr / MAX_R, j = pr % MAX_R;
+      float tval = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < MAX_S; ++sl) tval += tp[i][sl];
+      ttab[pr] = tval;
+      if (blockIdx.x == 0 && m < p.M && j < p.r) p.T_save[m * p.r + j] = tval;
+    }
+  }
+  __syncthreads();   // every wave has left the stream, and T is complete
+
+  // ---- the LoRA term of tile t, bf16(s T) B^T (contraction over the
+  //      ranks, 32 per MFMA: lane (i, g) holds bf16(s T[i][32 c + 8 g ..])
+  //      and B[n0 + 16 t + i][32 c + 8 g ..]), goes into wave t's sums ----
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    if (wave != t) continue;
+    f32x4_t lt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (uint32_t c = 0; c < RP / 32u; ++c) {
+      const f32x4_t* tr = reinterpret_cast<const f32x4_t*>(ttab + i16 * MAX_R + 32u * c + 8u * (uint32_t)g);
+      const f32x4_t ta = tr[0], tb = tr[1];
+      const u32x4v tv = {pack_bf16x2(p.s * ta[0], p.s * ta[1]), pack_bf16x2(p.s * ta[2], p.s * ta[3]),
+                         pack_bf16x2(p.s * tb[0], p.s * tb[1]), pack_bf16x2(p.s * tb[2], p.s * tb[3])};
+      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(btab + (uint32_t)(16 * t + i16) * BP + 32u * c +
+                                                             8u * (uint32_t)g);
+      lt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tv), bv, lt, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][e] += lt[e];
+  }
+
+  // ---- sums over the waves (fixed order), store ----
 #pragma unroll
   for (int t = 0; t < TR; ++t)
 #pragma unroll
@@ -399,12 +485,10 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     const uint32_t n = n0 + (uint32_t)c;
     if (n >= N) continue;
     const int t = c >> 4, ci = c & 15;
-    float base = 0.0f;
+    float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) base += red[(w * TR + t) * 256 + m * 16 + ci];
-    float lora = 0.0f;
-    for (int j = 0; j < p.r; ++j) lora += ttab[m * MAX_R + j] * bf16_to_f32(btab[c * p.r + j]);
-    p.Y[(size_t)m * N + n] = f32_to_bf16(base + p.s * lora);
+    for (int w = 0; w < WAVES; ++w) sum += red[(w * TR + t) * 256 + m * 16 + ci];
+    p.Y[(size_t)m * N + n] = f32_to_bf16(sum);
   }
 }
 
@@ -422,26 +506,27 @@ static int device_cus() {
   return n;
 }
 
+// dynamic LDS: the sums / restored scales, T [16][MAX_R] fp32, the
+// workgroup's rows of B [16 TR][BP] bf16
+static uint32_t dyn_lds(int TR, int r, uint32_t K) {
+  const uint32_t bp = (((uint32_t)r + 31u) & ~31u) + 8u;
+  return 4u * region0_floats(TR, K) + 4u * 16u * MAX_R + 2u * 16u * (uint32_t)TR * bp;
+}
+
 // Rows per workgroup: enough 16-row tiles (at most 7) that the grid is about
-// one workgroup per compute unit.
+// one workgroup per compute unit, and no more than the dynamic LDS and the
+// scale copy hold (K = 65536 allows two).
 struct Plan {
   int TR, RT;
 };
-static Plan plan(int64_t N, int r) {
+static Plan plan(int64_t N, int r, uint32_t K) {
   const int64_t cus = device_cus();
   Plan pl;
   pl.TR = (int)std::min<int64_t>(MAX_TR, std::max<int64_t>(1, (N + 16 * cus - 1) / (16 * cus)));
+  while (pl.TR > 1 && (dyn_lds(pl.TR, r, K) > (uint32_t)MAX_DYN_LDS || 16u * (uint32_t)pl.TR * (K / 64u) > QBYTES))
+    --pl.TR;
   pl.RT = (r + 15) / 16;
   return pl;
-}
-
-// dynamic LDS: per-wave sums [8][TR][256] and T [16][MAX_R] (fp32), which
-// in the stream hold the group constants [16 MAX_TR][2] (fp32) and the
-// scale bytes [16 TR][nbk]; then the workgroup's rows of B [16 TR][r] (bf16)
-static uint32_t dyn_lds(const Plan& pl, int r, uint32_t K) {
-  const uint32_t sums = 4u * ((uint32_t)WAVES * (uint32_t)pl.TR * 256u + 16u * MAX_R);
-  const uint32_t stream = 16u * 16u * MAX_TR + 16u * (uint32_t)pl.TR * (K / 64u);
-  return std::max(sums, stream) + 32u * (uint32_t)pl.TR * (uint32_t)r;
 }
 
 template <int TR, bool U8>
@@ -470,11 +555,11 @@ static hipError_t launch_tr(const Plan& pl, const DecArgs& p, unsigned grid, uin
 
 bool decode_fits(int64_t M, const NF4View& w, int r) {
   const int64_t lim = (int64_t)1 << 31;
-  // 32-bit buffer offsets; K a multiple of 256 and at most 16384 (a row's
-  // blocks lie in at most two groups of 256); 8-bit block scales (fp32
-  // scales take the tiled path); at most two 16-rank tiles of T
-  // (rows up to 16 * MAX_TR past N are addressed, and read as zeros)
-  return M >= 1 && M <= 16 && r >= 1 && r <= dec::MAX_R && w.K % 256 == 0 && w.K <= 16384 &&
+  // 32-bit buffer offsets; K a multiple of 256 (whole chunks for the eight
+  // waves) and at most MAX_K (one 16-row tile's restored scales fit the LDS
+  // and the scale copy); 8-bit block scales (fp32 scales take the tiled
+  // path) (rows up to 16 * MAX_TR past N are addressed, and read as zeros)
+  return M >= 1 && M <= 16 && r >= 1 && r <= dec::MAX_R && w.K % 256 == 0 && w.K <= dec::MAX_K &&
          !w.fp32_scale && (w.N + 16 * dec::MAX_TR) * (w.K / 2) + 1024 < lim &&
          (w.N + 16 * dec::MAX_TR) * (w.K / 64) + 1024 < lim && 16 * w.K * 2 < lim && (int64_t)r * w.K * 2 < lim &&
          w.N * r * 2 < lim && w.N * (w.K / 64) + 1024 < lim;
@@ -488,7 +573,10 @@ size_t decode_ws_bytes(int64_t K, int r) {
 
 hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A, const u16* B,
                          int r, float s, u16* Y, float* T_save, float* ws, hipStream_t st) {
-  const dec::Plan pl = dec::plan(w.N, r);
+  const dec::Plan pl = dec::plan(w.N, r, (uint32_t)w.K);
+  const uint32_t lds = dec::dyn_lds(pl.TR, r, (uint32_t)w.K);
+  if (lds > (uint32_t)dec::MAX_DYN_LDS || 16u * (uint32_t)pl.TR * ((uint32_t)w.K / 64u) > dec::QBYTES)
+    return hipErrorInvalidConfiguration;   // excluded by decode_fits and the plan; nothing launched
   const int S = dec::t_slices((uint32_t)w.K);
   hipLaunchKernelGGL(dec::k_decode_t, dim3((unsigned)S, (unsigned)pl.RT), dim3(256), 0, st, X, (int)M, A, r,
                      (uint32_t)w.K, S, pl.RT, ws);
@@ -504,7 +592,6 @@ hipError_t launch_decode(const NF4View& w, const u16* X, int64_t M, const u16* A
   p.B = B; p.r = r; p.s = s;
   p.Y = Y; p.T_save = T_save;
   const unsigned grid = (unsigned)((w.N + 16 * pl.TR - 1) / (16 * pl.TR));
-  const uint32_t lds = dec::dyn_lds(pl, r, (uint32_t)w.K);
   return w.u8_scale ? dec::launch_tr<true>(pl, p, grid, lds, st) : dec::launch_tr<false>(pl, p, grid, lds, st);
 }
 

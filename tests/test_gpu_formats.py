@@ -76,8 +76,9 @@ SHAPES = [
     # N, K, M, r, alpha
     (130, 320, 129, 17, 34.0),    # ragged tiles in every dimension
     (384, 512, 257, 64, 16.0),
-    (1000, 512, 3, 8, 16.0),      # decode size (the streaming kernel for E4M3 scales)
+    (1000, 512, 3, 8, 16.0),      # decode size (the streaming kernel, factored form)
     (4100, 2304, 7, 64, 16.0),    # decode size, T precomputed
+    (600, 8448, 5, 24, 16.0),     # decode size, K > 8192: the streaming kernel's exact form
 ]
 
 

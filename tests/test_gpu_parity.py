@@ -145,31 +145,37 @@ def test_fwd_bwd_small(orc, N, K, M, r, alpha):
 
 
 # decode-size forwards (M <= 16): the weight-streaming kernel over its plans
-# -- 16-row tiles per workgroup TR (1..16), tile groups TG (1..8) and
-# contraction ranges (8 / TG), one or two 16-rank tiles of T, ragged rows in
-# the last workgroup, ranges that hold no 256-wide step, more workgroups than
-# compute units -- and the shapes it leaves to the tiled kernels (r > 32,
-# K % 256 != 0)
+# -- 16-row tiles per workgroup TR (1..7, fewer where the restored block
+# scales would not fit the LDS or the scale copy), 128-wide contraction chunks dealt to eight
+# waves (fewer chunks than waves, a ragged last group of eight), one to eight
+# 16-rank tiles of T, ragged rows in the last workgroup, more workgroups than
+# compute units, contractions up to 65536 -- and the shape it leaves to the
+# tiled kernels (K % 256 != 0).  TR = min(7, ceil(N / (16 x 256 compute units))).
 DECODE = [
     # N, K, M, r, alpha
-    (1000, 512, 3, 8, 16.0),        # TR 1: two steps over eight ranges, ragged last workgroup
-    (4100, 2304, 7, 64, 16.0),      # r > 32: tiled kernels
-    (50, 768, 16, 128, 8.0),        # r > 32, fewer rows than one tile: tiled kernels
-    (2048, 11008, 16, 32, 32.0),    # two rank tiles, a group with no weight tile, 43 steps over 4 ranges
-    (28672, 1024, 1, 16, 32.0),     # TR 7, TG 4: the 70B-class row count
-    (40000, 256, 4, 24, 16.0),      # TR 10, TG 8, one step per wave
-    (12000, 4096, 16, 16, 32.0),    # TR 3, TG 2
+    (1000, 512, 3, 8, 16.0),        # TR 1, four chunks (four waves idle), ragged last workgroup
+    (4100, 2304, 7, 64, 16.0),      # rank 64 (four rank tiles of T), 18 chunks: a ragged group of two
+    (50, 768, 16, 128, 8.0),        # rank 128, fewer rows than one tile
+    (2048, 11008, 16, 32, 32.0),    # two rank tiles, 86 chunks: a ragged last group of six
+    (28672, 1024, 1, 16, 32.0),     # TR 7: the 70B-class row count, one chunk a wave
+    (40000, 256, 4, 24, 16.0),      # TR 7 (10 wanted), two chunks, 358 workgroups
+    (12000, 4096, 16, 16, 32.0),    # TR 3
     (4100, 4096, 9, 24, 16.0),      # TR 2, two rank tiles, ragged last tile
     (2000, 2048, 1, 8, 16.0),       # TR 1, a single token
-    (6000, 8192, 16, 64, 16.0),     # r > 32: tiled kernels
-    (1024, 16384, 1, 16, 32.0),     # long contraction, a single token
+    (6000, 8192, 16, 64, 16.0),     # TR 2 at rank 64
+    (1024, 16384, 1, 16, 32.0),     # long contraction (16 groups of chunks), a single token
     (3000, 16384, 9, 24, 16.0),     # long contraction, two rank tiles
-    (1001, 768, 5, 3, 16.0),        # odd N * r
+    (1001, 768, 5, 3, 16.0),        # odd N * r, six chunks
     (1001, 704, 5, 3, 16.0),        # K % 256 != 0: tiled kernels
-    (70000, 256, 2, 16, 16.0),      # TR capped at 16: more workgroups than compute units
+    (70000, 256, 2, 16, 16.0),      # TR 7, 625 workgroups: more than two a compute unit
     (4269, 4096, 4, 12, 16.0),      # TR 2, ragged rows
-    (20000, 512, 16, 17, 16.0),     # TR 5, TG 4, rank 17: the second rank tile holds one column
+    (20000, 512, 16, 17, 16.0),     # TR 5, rank 17: B rows element by element, one column in the second rank tile
     (8192, 8192, 16, 32, 16.0),     # the 8192 x 8192 layer at rank 32
+    (24576, 16384, 2, 16, 16.0),    # TR 6, exact form (K > 8192)
+    (2048, 28672, 16, 64, 16.0),    # the 70B down projection's contraction: rows span three scale groups
+    (1000, 65536, 3, 37, 16.0),     # the longest contraction (TR 1), rank 37
+    (28672, 4096, 5, 128, 16.0),    # TR 7 at rank 128 (eight rank tiles of T)
+    (5000, 1024, 16, 100, 8.0),     # rank 100: ranks padded to 128 with zeros
 ]
 
 
@@ -278,3 +284,11 @@ def test_workload_shapes(orc, key, li):
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_shapes(orc, li, M):
     _check_layer_full_size(orc, si.CONFIGS["decode_8192_28672"], li, M=M, bwd=False)
+
+
+@pytest.mark.parametrize("li", [0, 1])
+def test_decode_at_the_training_shapes(orc, li):
+    """The 70B-class up and down projections at 16 tokens and rank 64 (the
+    decode calls of the benchmark step; the down projection's contraction is
+    28672)."""
+    _check_layer_full_size(orc, si.CONFIGS["mlp70b_28672"], li, M=16, bwd=False)
