@@ -39,8 +39,8 @@
 // each code is looked up with byte permutes.  The even and the odd codes of
 // a register are looked up separately, so an operand holds its elements in
 // the order 0, 2, 4, 6, 1, 3, 5, 7; the X fragments (row m, the same 8
-// contraction indices) are permuted the same way.  Loads run D chunks
-// ahead in a register ring.  Since the waves run at the same pace, the two
+// contraction indices) are permuted the same way.  Loads run one chunk
+// ahead in a two-slot register ring.  Since the waves run at the same pace, the two
 // halves of each 128-byte line reach L2 close together and the line is
 // fetched from HBM once (measured: a wave that read both halves itself, one
 // chunk apart, fetched 1.7 times the weight's bytes).  The workgroups start
@@ -219,19 +219,15 @@ struct Chunk {
   bf16x8_t x[4];          // X[m = lane % 16][chunk offset 32 g + 8 v .. + 8], v = 0 .. 3
 };
 
-// Loads per chunk per wave, and D, the chunks loaded ahead: as deep as the
-// register ring allows (at most 160 of the 256 registers a wave of a
-// 512-lane workgroup may hold), at most 4, and within the 6-bit load
-// counter.
+// Loads per chunk per wave, and D, the chunks loaded ahead.  One: a wave
+// takes longer to dequantize and multiply a chunk than the chunk's loads take
+// to arrive, and a deeper ring only lengthens the start, where every
+// workgroup's first requests arrive together (measured: D = 2 and the earlier
+// register-budget depths were 4-20% slower than D = 1).
 template <int TR>
 constexpr int lpc_of() { return TR + 4; }
 template <int TR>
-constexpr int depth_of() {
-  constexpr int slot = 4 * TR + 16;          // registers of one ring slot
-  int d = 160 / slot - 1;                    // the ring takes at most 160
-  d = d < 1 ? 1 : d > 4 ? 4 : d;
-  return d * lpc_of<TR>() > 60 ? 60 / lpc_of<TR>() : d;
-}
+constexpr int depth_of() { return 1; }
 
 template <int TR, bool U8>
 __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
