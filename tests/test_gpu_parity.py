@@ -176,6 +176,7 @@ DECODE = [
     (1000, 65536, 3, 37, 16.0),     # the longest contraction (TR 1), rank 37
     (28672, 4096, 5, 128, 16.0),    # TR 7 at rank 128 (eight rank tiles of T)
     (5000, 1024, 16, 100, 8.0),     # rank 100: ranks padded to 128 with zeros
+    (1007, 4096, 9, 36, 16.0),      # 15 rows in the last tile, rank 36: B rows element by element
 ]
 
 
