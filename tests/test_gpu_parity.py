@@ -291,5 +291,22 @@ def test_decode_shapes(orc, li, M):
 def test_decode_at_the_training_shapes(orc, li):
     """The 70B-class up and down projections at 16 tokens and rank 64 (the
     decode calls of the benchmark step; the down projection's contraction is
-    28672)."""
-    _check_layer_full_size(orc, si.CONFIGS["mlp70b_28672"], li, M=16, bwd=False)
+    28672), every output against the oracle.  The decode kernel multiplies the
+    exactly dequantized weight, so its elementwise error stays far inside the
+    tolerance (about a fifth of it here): rounding the unscaled level to bf16
+    and scaling each block's partial sum instead reaches 1.5 times the bound
+    on the up projection, whose weights have outliers, and would fail the
+    stricter check below."""
+    from helpers import ELEM_ABS
+    cfg = si.CONFIGS["mlp70b_28672"]
+    lay = GpuLayer(cfg, li, M=16, quantize=False)
+    label = f"{cfg.key}/{cfg.layers[li].name} M=16"
+    w, Wdq = check_quantize(orc, lay.W, label)
+    log(f"[decode fwd] {label} r={lay.r}")
+    Y, T = q.qlora_linear_fwd(w, lay.dX_in, lay.dA_in, lay.dB_in, lay.alpha)
+    torch.cuda.synchronize()
+    Yr, Tr = orc.qlora_fwd(Wdq, lay.X, lay.A, lay.B, lay.alpha)
+    assert_close(tensor_f64(T), Tr, f"{label} T")
+    assert_close(tensor_f64(Y), Yr, f"{label} Y")
+    worst = float(np.max(np.abs(tensor_f64(Y) - Yr) / (ELEM_ABS * (1.0 + np.abs(Yr)))))
+    assert worst <= 0.5, f"{label}: elementwise error at {worst:.3f} of the bound (exact weights give about 0.2)"
