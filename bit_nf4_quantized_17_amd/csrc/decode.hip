@@ -18,8 +18,8 @@
 // (S x RT small workgroups, fp32 partials in the workspace).  The second
 // streams the weight with no communication between workgroups: a workgroup
 // owns 16 * TR consecutive output columns (W rows, TR <= 7) over the whole
-// contraction, so it finishes its outputs itself; at the end it adds up the
-// S partials of T in a fixed order for its LoRA term.  Its grid is about one
+// contraction, so it finishes its outputs itself; at the start it adds up
+// the S partials of T in a fixed order for its LoRA term.  Its grid is about one
 // workgroup per compute unit.  The 8-bit block scales of its rows are one
 // contiguous run of bytes; at the start it restores them into an fp32 table
 // in LDS, so a row's blocks may span any number of scale groups.
@@ -46,9 +46,9 @@
 // chunk apart, fetched 1.7 times the weight's bytes).  The workgroups start
 // at different groups of chunks (if every workgroup read the same column
 // window of its rows at the same time, the requests would pile onto a few
-// memory channels).  The eight waves' sums are added in LDS in wave order
-// (wave t first adds the LoRA term of tile t to its own), so results do not
-// depend on timing.
+// memory channels).  Wave t starts its sums of tile t from the LoRA term,
+// and the eight waves' sums are added in LDS in wave order, so results do
+// not depend on timing.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -73,10 +73,16 @@ constexpr int QPASS = 4;                // 16-byte scale loads a thread
 constexpr uint32_t QBYTES = 16u * NTHREADS * QPASS;   // scale bytes a workgroup can restore (32 KB)
 constexpr int BCH = (16 * MAX_TR * (MAX_R + 8) / 8 + NTHREADS - 1) / NTHREADS;   // 16-byte B chunks a thread
 
+// Row pitch of the restored block scales in LDS: K / 64 is a multiple of 4,
+// so K / 64 + 2 is twice an odd number and the sixteen rows a lane group
+// reads at one block index fall on sixteen different banks (a pitch of
+// K / 64 put them all on one bank).
+__host__ __device__ inline uint32_t scale_pitch(uint32_t K) { return K / 64u + 2u; }
+
 // floats at the start of the dynamic LDS: the per-wave sums [8][TR][256]
-// after the stream, the restored block scales [16 TR][K / 64] during it
+// after the stream, the restored block scales [16 TR][scale_pitch] during it
 __host__ __device__ inline uint32_t region0_floats(int TR, uint32_t K) {
-  const uint32_t sums = (uint32_t)WAVES * 256u, scales = 16u * (K / 64u);
+  const uint32_t sums = (uint32_t)WAVES * 256u, scales = 16u * scale_pitch(K);
   return (sums > scales ? sums : scales) * (uint32_t)TR;
 }
 
@@ -333,8 +339,24 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     }
   }
 
-  // ---- prologue: the first D chunks, each group of loads kept whole and
-  //      in order (the waits below count loads per chunk) ----
+  // ---- T = the sum of its partials in slice order, [16 m][MAX_R] (ranks
+  //      past r and rows past M hold zero): the loads go out now, before the
+  //      first chunk's, and are summed while the chunk is on its way ----
+  const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)p.RT);
+  constexpr int TP = 16 * MAX_R / NTHREADS;
+  float tp[TP][MAX_S];
+#pragma unroll
+  for (int i = 0; i < TP; ++i) {
+    const uint32_t pr = (uint32_t)(tid + NTHREADS * i), m = pr / MAX_R, j = pr % MAX_R;
+#pragma unroll
+    for (int sl = 0; sl < MAX_S; ++sl)
+      tp[i][sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rT, sl < p.S && j < (uint32_t)p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)p.RT + j) : OOB,
+          0, 0));
+  }
+
+  // ---- the first D chunks, each group of loads kept whole and in order
+  //      (the waits below count loads per chunk) ----
   Chunk<TR> f[NS];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -343,11 +365,13 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // The restored scales and the rows of B go to LDS now (their loads are
-  // older than the prologue's); the scales share the space of the per-wave
-  // sums, which are written only after every wave has left the stream
+  // The restored scales, T and the rows of B go to LDS now (their loads are
+  // older than the first chunk's); the scales share the space of the
+  // per-wave sums, which are written only after every wave has left the
+  // stream
+  const uint32_t SP = scale_pitch(K);
   float* red = reinterpret_cast<float*>(smem);                 // [8 waves][TR][16 m][16 n]
-  float* stab = red;                                           // [16 TR rows][nbk] block scales
+  float* stab = red;                                           // [16 TR rows][SP] block scales
   float* ttab = red + region0_floats(TR, K);                   // [16 m][MAX_R]
   u16* btab = reinterpret_cast<u16*>(ttab + 16 * MAX_R);       // B rows of the workgroup [16 TR][BP]
   wait_vm<LPC * D>();
@@ -357,7 +381,8 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     if (q < bchunks) *reinterpret_cast<u32x4v*>(btab + 8u * q) = bch[i];
   }
   // s_b = fl32(v(q_b) * d_g): v the E4M3 value of the byte, or the byte as an
-  // integer for uint8-linear scales
+  // integer for uint8-linear scales.  Scale j of the run is row j / nbk,
+  // block j % nbk; four consecutive scales from a multiple of 4 share a row.
 #pragma unroll
   for (int i = 0; i < QPASS; ++i) {
     const uint32_t o = 16u * (uint32_t)(tid + NTHREADS * i);
@@ -365,36 +390,68 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t q = qv[i][w];
-        u32x4v sv;
+        const uint32_t j = o + 4u * (uint32_t)w, row = j / nbk;
+        float sv[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const uint32_t qb = q >> (8 * b);
           const float v = U8 ? (float)(qb & 0xFFu) : __builtin_amdgcn_cvt_f32_fp8((int)qb, 0);
-          sv[b] = __float_as_uint(v * qd[i]);
+          sv[b] = v * qd[i];
         }
-        *reinterpret_cast<u32x4v*>(stab + o + 4u * (uint32_t)w) = sv;
+        float* dst = stab + j + 2u * row;   // row * SP + j % nbk, 8-byte aligned
+        reinterpret_cast<float2*>(dst)[0] = float2{sv[0], sv[1]};
+        reinterpret_cast<float2*>(dst)[1] = float2{sv[2], sv[3]};
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < TP; ++i) {
+    const int pr = tid + NTHREADS * i, m = pr / MAX_R, j = pr % MAX_R;
+    float tval = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < MAX_S; ++sl) tval += tp[i][sl];
+    ttab[pr] = tval;
+    if (blockIdx.x == 0 && m < p.M && j < p.r) p.T_save[m * p.r + j] = tval;
+  }
 
-  __syncthreads();   // the restored scales are complete
+  __syncthreads();   // the restored scales, T and B are complete
 
+  // ---- the LoRA term of tile t, bf16(s T) B^T (contraction over the
+  //      ranks, 32 per MFMA: lane (i, g) holds bf16(s T[i][32 c + 8 g ..])
+  //      and B[n0 + 16 t + i][32 c + 8 g ..]), starts wave t's sums of tile
+  //      t; the stream's products are added to it ----
   f32x4_t acc[TR];
 #pragma unroll
-  for (int t = 0; t < TR; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TR; ++t) {
+    acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (wave != t) continue;
+    for (uint32_t c = 0; c < RP / 32u; ++c) {
+      const f32x4_t* tr = reinterpret_cast<const f32x4_t*>(ttab + i16 * MAX_R + 32u * c + 8u * (uint32_t)g);
+      const f32x4_t ta = tr[0], tb = tr[1];
+      const u32x4v tv = {pack_bf16x2(p.s * ta[0], p.s * ta[1]), pack_bf16x2(p.s * ta[2], p.s * ta[3]),
+                         pack_bf16x2(p.s * tb[0], p.s * tb[1]), pack_bf16x2(p.s * tb[2], p.s * tb[3])};
+      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(btab + (uint32_t)(16 * t + i16) * BP + 32u * c +
+                                                             8u * (uint32_t)g);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tv), bv, acc[t], 0, 0, 0);
+    }
+  }
 
   auto process = [&](const Chunk<TR>& f, int i) {
     if (i >= G) return;
     const int c = chunk_of(i);
     if (c >= C) return;
-    // the lane's block within the row: two per chunk, lane groups 0, 1 in the first
+    // the lane's block within the row: two per chunk, lane groups 0, 1 in the
+    // first; the chunk's block scales of every tile are read up front
     const uint32_t kb = 2u * (uint32_t)c + ((uint32_t)g >> 1);
+    float sc[TR];
+#pragma unroll
+    for (int t = 0; t < TR; ++t) sc[t] = stab[(uint32_t)(16 * t + i16) * SP + kb];
     bf16x8_t xp[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) xp[v] = evens_then_odds(f.x[v]);
 #pragma unroll
     for (int t = 0; t < TR; ++t) {
-      const Table tb = make_table(lv8, stab[(uint32_t)(16 * t + i16) * nbk + kb]);
+      const Table tb = make_table(lv8, sc[t]);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[0], dequant8(tb, f.c[t].x), acc[t], 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[1], dequant8(tb, f.c[t].y), acc[t], 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[2], dequant8(tb, f.c[t].z), acc[t], 0, 0, 0);
@@ -419,53 +476,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     }
   }
   wait_vm<0>();
-
-  // ---- T = the sum of the partials in slice order, [16 m][MAX_R] (ranks
-  //      past r and rows past M hold zero); workgroup 0 also stores it ----
-  {
-    const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)p.RT);
-    constexpr int TP = 16 * MAX_R / NTHREADS;
-    float tp[TP][MAX_S];
-#pragma unroll
-    for (int i = 0; i < TP; ++i) {
-      const uint32_t pr = (uint32_t)(tid + NTHREADS * i), m = pr / MAX_R, j = pr % MAX_R;
-#pragma unroll
-      for (int sl = 0; sl < MAX_S; ++sl)
-        tp[i][sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rT, sl < p.S && j < (uint32_t)p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)p.RT + j) : OOB,
-            0, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < TP; ++i) {
-      const int pr = tid + NTHREADS * i, m = pr / MAX_R, j = pr % MAX_R;
-      float tval = 0.0f;
-#pragma unroll
-      for (int sl = 0; sl < MAX_S; ++sl) tval += tp[i][sl];
-      ttab[pr] = tval;
-      if (blockIdx.x == 0 && m < p.M && j < p.r) p.T_save[m * p.r + j] = tval;
-    }
-  }
-  __syncthreads();   // every wave has left the stream, and T is complete
-
-  // ---- the LoRA term of tile t, bf16(s T) B^T (contraction over the
-  //      ranks, 32 per MFMA: lane (i, g) holds bf16(s T[i][32 c + 8 g ..])
-  //      and B[n0 + 16 t + i][32 c + 8 g ..]), goes into wave t's sums ----
-#pragma unroll
-  for (int t = 0; t < TR; ++t) {
-    if (wave != t) continue;
-    f32x4_t lt = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (uint32_t c = 0; c < RP / 32u; ++c) {
-      const f32x4_t* tr = reinterpret_cast<const f32x4_t*>(ttab + i16 * MAX_R + 32u * c + 8u * (uint32_t)g);
-      const f32x4_t ta = tr[0], tb = tr[1];
-      const u32x4v tv = {pack_bf16x2(p.s * ta[0], p.s * ta[1]), pack_bf16x2(p.s * ta[2], p.s * ta[3]),
-                         pack_bf16x2(p.s * tb[0], p.s * tb[1]), pack_bf16x2(p.s * tb[2], p.s * tb[3])};
-      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(btab + (uint32_t)(16 * t + i16) * BP + 32u * c +
-                                                             8u * (uint32_t)g);
-      lt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tv), bv, lt, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[t][e] += lt[e];
-  }
+  __syncthreads();   // every wave has left the stream (the scales' space is reused)
 
   // ---- sums over the waves (fixed order), store ----
 #pragma unroll
