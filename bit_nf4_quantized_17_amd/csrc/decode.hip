@@ -270,13 +270,17 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   // ---- the workgroup's block scales, 16 TR nbk contiguous bytes from
   //      n0 nbk (at most QBYTES), 16 bytes a thread and pass, with the group
   //      constant of each thread's 16 (n0 nbk is a multiple of 16, so they
-  //      lie in one group of 256); rows past N read zeros ----
+  //      lie in one group of 256); rows past N read zeros
   const uint32_t qbytes = 16u * (uint32_t)TR * nbk;
   const auto rD = rsrc(p.dscale, 4u * ((N * nbk + 255u) / 256u));
+  //      (a wave whose 16-byte pieces all lie past the run issues nothing) ----
   u32x4v qv[QPASS];
   float qd[QPASS];
 #pragma unroll
   for (int i = 0; i < QPASS; ++i) {
+    qv[i] = u32x4v{0u, 0u, 0u, 0u};
+    qd[i] = 0.0f;
+    if (16u * (uint32_t)(64 * wave + NTHREADS * i) >= qbytes) continue;
     const uint32_t o = 16u * (uint32_t)(tid + NTHREADS * i);
     qv[i] = __builtin_amdgcn_raw_buffer_load_b128(rQ, o < qbytes ? n0 * nbk + o : OOB, 0, 0);
     qd[i] = __uint_as_float(
@@ -320,6 +324,8 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   u32x4v bch[BCH];
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
+    bch[i] = u32x4v{0u, 0u, 0u, 0u};
+    if ((uint32_t)(64 * wave + NTHREADS * i) >= bchunks) continue;   // nothing of this wave's
     const uint32_t q = (uint32_t)(tid + NTHREADS * i);
     const uint32_t c = q / BQ, j0 = 8u * (q - c * BQ);
     const uint32_t row0 = ((n0 + c) * (uint32_t)p.r + j0) * 2u;   // byte offset of (row, j0)
@@ -339,20 +345,28 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     }
   }
 
-  // ---- T = the sum of its partials in slice order, [16 m][MAX_R] (ranks
-  //      past r and rows past M hold zero): the loads go out now, before the
-  //      first chunk's, and are summed while the chunk is on its way ----
+  // ---- T = the sum of its partials in slice order, kept [16 m][MAX_R] in
+  //      LDS; entry e = (m, j) of [16][RP] is thread e % NTHREADS's, and
+  //      ranks past r and rows past M hold zero.  The loads go out now,
+  //      before the first chunk's, and are summed while the chunk is on its
+  //      way; a wave whose entries all lie in rows past M, and every slice
+  //      past S, issues nothing. ----
   const auto rT = rsrc(p.tpart, 4u * (uint32_t)p.S * 256u * (uint32_t)p.RT);
   constexpr int TP = 16 * MAX_R / NTHREADS;
+  const uint32_t RW = 16u * (uint32_t)p.RT;   // width of a partial's rows
   float tp[TP][MAX_S];
 #pragma unroll
   for (int i = 0; i < TP; ++i) {
-    const uint32_t pr = (uint32_t)(tid + NTHREADS * i), m = pr / MAX_R, j = pr % MAX_R;
+    const uint32_t e = (uint32_t)(tid + NTHREADS * i), m = e / RP, j = e - m * RP;
+    const uint32_t e0 = (uint32_t)(64 * wave + NTHREADS * i);
+    const bool wave_live = e0 < 16u * RP && e0 / RP < (uint32_t)p.M;
 #pragma unroll
-    for (int sl = 0; sl < MAX_S; ++sl)
+    for (int sl = 0; sl < MAX_S; ++sl) {
+      tp[i][sl] = 0.0f;
+      if (!wave_live || sl >= p.S) continue;
       tp[i][sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rT, sl < p.S && j < (uint32_t)p.r ? 4u * (((uint32_t)sl * 16u + m) * 16u * (uint32_t)p.RT + j) : OOB,
-          0, 0));
+          rT, m < (uint32_t)p.M && j < (uint32_t)p.r ? 4u * (((uint32_t)sl * 16u + m) * RW + j) : OOB, 0, 0));
+    }
   }
 
   // ---- the first D chunks, each group of loads kept whole and in order
@@ -406,12 +420,13 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   }
 #pragma unroll
   for (int i = 0; i < TP; ++i) {
-    const int pr = tid + NTHREADS * i, m = pr / MAX_R, j = pr % MAX_R;
+    const uint32_t e = (uint32_t)(tid + NTHREADS * i), m = e / RP, j = e - m * RP;
+    if (e >= 16u * RP) continue;
     float tval = 0.0f;
 #pragma unroll
     for (int sl = 0; sl < MAX_S; ++sl) tval += tp[i][sl];
-    ttab[pr] = tval;
-    if (blockIdx.x == 0 && m < p.M && j < p.r) p.T_save[m * p.r + j] = tval;
+    ttab[m * MAX_R + j] = tval;
+    if (blockIdx.x == 0 && m < (uint32_t)p.M && j < (uint32_t)p.r) p.T_save[m * (uint32_t)p.r + j] = tval;
   }
 
   __syncthreads();   // the restored scales, T and B are complete
