@@ -216,6 +216,25 @@ def test_zero_B_gives_bitwise_base_output(orc):
     assert float(dA.float().abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("M", [1, 16])
+def test_zero_B_gives_bitwise_base_output_at_decode_sizes(orc, M):
+    # the decode kernel starts its sums from the LoRA term: with B = 0 that term
+    # is exactly zero, so alpha and A must not change a bit of the output
+    cfg = si.custom(N=384, K=512, M=M, r=16, alpha=32.0, seed=5)
+    lay = GpuLayer(cfg)
+    log(f"[decode] zero-B invariant, M = {M}")
+    Bz = torch.zeros_like(lay.dB_in)
+    Y0, T0 = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, Bz, 32.0)
+    Ya, _ = q.qlora_linear_fwd(lay.w, lay.dX_in, lay.dA_in, lay.dB_in, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.float(), Ya.float())   # equal values (+0 and -0 alike)
+    assert float(T0.abs().max()) > 0.0          # T itself is not zero
+    codes, qs, ds = _quant_host(lay.w)
+    Wdq = orc.nf4_dequantize(codes, qs, ds, lay.N, lay.K)
+    Yr, _ = orc.qlora_fwd(Wdq, lay.X, lay.A, lay.B, 0.0)
+    assert_close(tensor_f64(Y0), Yr, "Y base")
+
+
 def test_bwd_variants_agree_and_are_deterministic(orc):
     cfg = si.custom(N=320, K=256, M=200, r=24, alpha=16.0, seed=5)
     lay = GpuLayer(cfg)
