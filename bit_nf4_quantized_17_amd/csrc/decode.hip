@@ -217,12 +217,12 @@ __device__ __forceinline__ bf16x8_t evens_then_odds(bf16x8_t x) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-// One wave's register loads of one chunk: per tile the codes of the lane's
-// row, and the X fragments of the chunk's four MFMAs (shared by every tile).
+// One wave's register loads of one chunk: the X fragments of the chunk's four
+// MFMAs (shared by every tile), then per tile the codes of the lane's row.
 template <int TR>
 struct Chunk {
-  u32x4v c[TR];           // row n0 + 16 t + lane % 16, code bytes [16 g, 16 g + 16) of the chunk
   bf16x8_t x[4];          // X[m = lane % 16][chunk offset 32 g + 8 v .. + 8], v = 0 .. 3
+  u32x4v c[TR];           // row n0 + 16 t + lane % 16, code bytes [16 g, 16 g + 16) of the chunk
 };
 
 // Loads per chunk per wave, and D, the chunks loaded ahead.  One: a wave
@@ -298,11 +298,11 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
     // (the tile's offset goes into the per-lane offset, which is what the
     // buffer range check sees)
 #pragma unroll
-    for (int t = 0; t < TR; ++t)
-      f.c[t] = __builtin_amdgcn_raw_buffer_load_b128(rC, co + 16u * (uint32_t)t * RB, 0, 0);
-#pragma unroll
     for (int v = 0; v < 4; ++v)
       f.x[v] = ld16(rX, xoff + 256u * c + 16u * (uint32_t)v);
+#pragma unroll
+    for (int t = 0; t < TR; ++t)
+      f.c[t] = __builtin_amdgcn_raw_buffer_load_b128(rC, co + 16u * (uint32_t)t * RB, 0, 0);
   };
 
   // ---- this lane's eight levels, 0 .. 7 in even 16-lane rows and 8 .. 15
@@ -476,9 +476,10 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
 
   // ---- the stream: chunks in groups of NS so that the register ring is
   //      indexed by constants.  At chunk i the loads of chunk i + D go out
-  //      into the slot that chunk i - 1 used, and once this wave's loads of
-  //      chunk i have landed (D later chunks may still be in flight) it is
-  //      multiplied. ----
+  //      into the slot that chunk i - 1 used, and chunk i is multiplied as it
+  //      lands: a chunk's X fragments are loaded before its tiles, and each
+  //      use of a loaded register waits only for its own load, so tile 0 is
+  //      dequantized while the later tiles are still arriving. ----
   for (int i0 = 0; i0 < G; i0 += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -486,8 +487,8 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       issue(f[(j + D) % NS], i + D);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<LPC * D>();
-      process(f[j], i);            // nothing past the last iteration or past C
+      process(f[j], i);            // nothing past the last iteration or past C; each use of a
+                                   // loaded register waits for its own load (X, then tile by tile)
     }
   }
   wait_vm<0>();
