@@ -74,7 +74,7 @@ def _check(orc, cases, lr, b1, b2, eps, wd, step):
         assert np.all(np.abs(gp - th) <= 0.5 * _ulp_bf16(gp) + tol), f"n={c.n}: param"
 
 
-SIZES = [1, 7, 8, 9, 2047, 2048, 2049, 64 * 8192, 1000 * 64 + 3]
+SIZES = [1, 7, 8, 9, 2047, 2048, 2049, 4095, 4096, 4097, 6151, 64 * 8192, 1000 * 64 + 3]
 
 
 @pytest.mark.parametrize("step", [1, 3, 1000])
