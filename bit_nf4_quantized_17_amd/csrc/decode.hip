@@ -270,10 +270,10 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   // ---- the workgroup's block scales, 16 TR nbk contiguous bytes from
   //      n0 nbk (at most QBYTES), 16 bytes a thread and pass, with the group
   //      constant of each thread's 16 (n0 nbk is a multiple of 16, so they
-  //      lie in one group of 256); rows past N read zeros
+  //      lie in one group of 256); rows past N read zeros, and a wave whose
+  //      16-byte pieces all lie past the run issues nothing ----
   const uint32_t qbytes = 16u * (uint32_t)TR * nbk;
   const auto rD = rsrc(p.dscale, 4u * ((N * nbk + 255u) / 256u));
-  //      (a wave whose 16-byte pieces all lie past the run issues nothing) ----
   u32x4v qv[QPASS];
   float qd[QPASS];
 #pragma unroll
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NTHREADS) void k_decode(DecArgs p) {
   // issue iteration i's chunk into a ring slot.  Past the last iteration,
   // or past C in a ragged group, a wave reloads a chunk it has (an L2 hit)
   // rather than selecting other offsets, so that every iteration issues the
-  // same loads from one code path and the waits below are constants.
+  // same loads from one code path (the waits count loads in issue order).
   auto issue = [&](Chunk<TR>& f, int i) {
     const int cc = chunk_of(i < G ? i : G - 1);
     const uint32_t c = (uint32_t)(cc < C ? cc : C - 1);
